@@ -1,0 +1,82 @@
+// Internal declarations shared by the host-side sources of libecf.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "../../include/ecf.h"
+
+namespace ecf {
+
+// ---- errors -------------------------------------------------------------------
+int set_error(int code, const char *fmt, ...);
+#define ECF_HIP_CHECK(expr)                                                                   \
+    do {                                                                                      \
+        hipError_t _e = (expr);                                                               \
+        if (_e != hipSuccess)                                                                 \
+            return ::ecf::set_error(ECF_EHIP, "%s failed: %s (%s:%d)", #expr,                \
+                                    hipGetErrorString(_e), __FILE__, __LINE__);               \
+    } while (0)
+
+// ---- profiling (event pairs around launches) ------------------------------------
+struct ProfScope {
+    ProfScope(const char *name, hipStream_t s);
+    ~ProfScope();
+    const char *name_;
+    hipStream_t s_;
+    hipEvent_t a_ = nullptr, b_ = nullptr;
+};
+
+// ---- geometry ------------------------------------------------------------------
+constexpr int kSortSeg = 1024;      // rows per segment of the multi-block counting sort
+constexpr int kSmallRouteRows = 2048; // R up to this uses the single-block routing kernel
+constexpr int kPrefillMT = 128;     // rows per prefill GEMM tile
+constexpr int kDecodeNT = 2;        // max rows per pass of the decode GEMV kernels
+
+struct BlobLayout {
+    size_t off[6];  // w_gate, w_up, w_down, s_gate, s_up, s_down
+    size_t bytes;
+};
+bool blob_layout(const ecf_shape &s, BlobLayout *out);
+
+// Workspace carve-up for up to T tokens.
+struct WsLayout {
+    size_t logits, idx, gate, counts, offsets, perm, pos, active, n_active, tiles, n_tiles,
+        seg_counts, seg_base, ptrs, hbuf, ybuf, host_out, total;
+};
+WsLayout ws_layout(const ecf_shape &s, int32_t T);
+int max_tiles(const ecf_shape &s, int32_t T);
+
+// ---- kernel launchers (k_*.hip) -------------------------------------------------
+struct RouteOut {
+    int32_t *idx;
+    float *gate;
+    int32_t *counts, *offsets, *perm, *pos, *active, *n_active, *tiles, *n_tiles;
+    int32_t *seg_counts, *seg_base;
+};
+
+int launch_router_logits(const ecf_shape &s, const void *x, const void *wr, int T, float *logits,
+                         hipStream_t st);
+int launch_route(const ecf_shape &s, const float *logits, int T, const RouteOut &o, hipStream_t st);
+
+struct ExpertTables {
+    const uint64_t *ptrs;  // [E] device blob addresses (0 = not evaluated on the GPU)
+    BlobLayout lay;
+};
+
+int launch_decode_gateup(const ecf_shape &s, const ExpertTables &ex, const RouteOut &o, const void *x,
+                         int T, float *H, hipStream_t st);
+int launch_decode_down(const ecf_shape &s, const ExpertTables &ex, const RouteOut &o, const float *H,
+                       int T, float *Y, hipStream_t st);
+int launch_prefill_gemm1(const ecf_shape &s, const ExpertTables &ex, const RouteOut &o, const void *x,
+                         int T, uint16_t *H, hipStream_t st);
+int launch_prefill_gemm2(const ecf_shape &s, const ExpertTables &ex, const RouteOut &o, const uint16_t *H,
+                         int T, float *Y, hipStream_t st);
+int launch_combine(const ecf_shape &s, const ExpertTables &ex, const RouteOut &o, const float *Y, int T,
+                   const float *residual, const float *host_part, float *out, void *out_act,
+                   hipStream_t st);
+
+}  // namespace ecf

@@ -1,0 +1,49 @@
+// Host-core evaluation of experts assigned to the CPU by the q* split.
+#pragma once
+
+#include <atomic>
+#include <condition_variable>
+#include <cstdint>
+#include <functional>
+#include <mutex>
+#include <thread>
+#include <vector>
+
+#include "ecf_internal.h"
+
+namespace ecf {
+
+// Fixed pool of worker threads; parallel_for runs fn(0..n-1) on the workers
+// and the calling thread and returns when every index is done.
+class HostPool {
+public:
+    explicit HostPool(int n_threads);
+    ~HostPool();
+    int size() const { return (int)th_.size() + 1; }
+    void parallel_for(int n, const std::function<void(int)> &fn);
+
+private:
+    void worker();
+    std::vector<std::thread> th_;
+    std::mutex mu_;
+    std::condition_variable cv_, done_cv_;
+    const std::function<void(int)> *fn_ = nullptr;
+    std::atomic<int> next_{0};
+    int total_ = 0, busy_ = 0;
+    uint64_t epoch_ = 0;
+    bool stop_ = false;
+};
+
+struct HostExpertJob {
+    int expert;
+    const void *blob;       // pinned host blob of this (layer, expert)
+    std::vector<int> rows;  // flat routed rows f = t*k + j sent to this expert
+};
+
+// y[f][:] = W_down . (silu(W_gate . x[t]) * (W_up . x[t])) for every row f of
+// every job, t = f / k.  x: host [T][d] in a_dtype; weights fp32 or bf16.
+// Math in fp32 with 16 independent partial sums per dot product.
+int host_experts(HostPool &pool, const ecf_shape &s, const BlobLayout &lay,
+                 const std::vector<HostExpertJob> &jobs, const void *x, int T, float *y);
+
+}  // namespace ecf

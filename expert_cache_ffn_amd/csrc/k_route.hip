@@ -1,0 +1,477 @@
+// Routing kernels: router logits (fp64-accumulated GEMV), wave-level top-k with
+// softmax gates, and the stable counting-sort permutation of routed rows.
+//
+// The router activates k of the E experts per token (FreeToken paper
+// explainer, section "MoE opens one door and closes another"); the softmax
+// gating and the sort are the standard definitions, with these readings:
+//  * logits are exact products summed in fp64 and rounded once to fp32, the
+//    precision the top-k decision is taken in;
+//  * top-k order is logit descending, ties to the lower expert id; NaN logits
+//    rank as -inf;
+//  * gates are the softmax over the k selected logits (renorm = 1) or the
+//    full softmax probabilities at the selected experts (renorm = 0);
+//  * the permutation lists the rows f = t*k + j of expert 0, then 1, ...,
+//    each group in ascending f (a stable sort by expert).
+#include <climits>
+
+#include "device_common.h"
+#include "ecf_internal.h"
+
+namespace ecf {
+
+// ---------------------------------------------------------------------------------
+// Router GEMV.  Block = one expert x TT tokens; its 4 waves interleave over d in
+// 16-byte vectors.  grid = (E, ceil(T / TT)).
+template <bool BF16, int TT>
+__global__ __launch_bounds__(256) void k_router_logits(const void *__restrict__ x,
+                                                       const void *__restrict__ wr, int T, int d,
+                                                       int E, float *__restrict__ logits)
+{
+    __shared__ double red[4][TT];
+    const int e = blockIdx.x, t0 = blockIdx.y * TT;
+    const int nt = min(TT, T - t0);
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    constexpr int V = BF16 ? 8 : 4;
+    double acc[TT];
+#pragma unroll
+    for (int q = 0; q < TT; ++q)
+        acc[q] = 0.0;
+    for (int c = threadIdx.x * V; c < d; c += 256 * V) {
+        float wv[V], xv[V];
+        if (BF16) {
+            uint4 u = *reinterpret_cast<const uint4 *>((const uint16_t *)wr + (size_t)e * d + c);
+            uint32_t p[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                wv[2 * i] = bf_lo(p[i]);
+                wv[2 * i + 1] = bf_hi(p[i]);
+            }
+        } else {
+            float4 u = *reinterpret_cast<const float4 *>((const float *)wr + (size_t)e * d + c);
+            wv[0] = u.x, wv[1] = u.y, wv[2] = u.z, wv[3] = u.w;
+        }
+#pragma unroll
+        for (int q = 0; q < TT; ++q) {
+            if (q < nt) {
+                if (BF16) {
+                    uint4 u = *reinterpret_cast<const uint4 *>((const uint16_t *)x + (size_t)(t0 + q) * d + c);
+                    uint32_t p[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        xv[2 * i] = bf_lo(p[i]);
+                        xv[2 * i + 1] = bf_hi(p[i]);
+                    }
+                } else {
+                    float4 u = *reinterpret_cast<const float4 *>((const float *)x + (size_t)(t0 + q) * d + c);
+                    xv[0] = u.x, xv[1] = u.y, xv[2] = u.z, xv[3] = u.w;
+                }
+#pragma unroll
+                for (int i = 0; i < V; ++i)
+                    acc[q] = fma((double)xv[i], (double)wv[i], acc[q]);  // product exact in fp64
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < TT; ++q) {
+        double v = wave_sum(acc[q]);
+        if (lane == 0)
+            red[w][q] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < nt) {
+        const int q = threadIdx.x;
+        double s = (red[0][q] + red[1][q]) + (red[2][q] + red[3][q]);
+        logits[(size_t)(t0 + q) * E + e] = (float)s;
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// Top-k of one token's logits by one wave.  MAXS = logits held per lane.
+template <int MAXS>
+__device__ __forceinline__ void topk_wave(const float *__restrict__ lg, int E, int k, int renorm,
+                                          int lane, int32_t *idx_out, float *gate_out, int *sidx)
+{
+    float v[MAXS];
+    uint32_t taken = 0;
+#pragma unroll
+    for (int s = 0; s < MAXS; ++s) {
+        const int e = lane + 64 * s;
+        float x = e < E ? lg[e] : -INFINITY;
+        if (x != x)
+            x = -INFINITY;
+        v[s] = x;
+        if (e >= E)
+            taken |= 1u << s;
+    }
+    float my_v = 0.f;
+    int my_e = 0;
+    for (int j = 0; j < k; ++j) {
+        float bv = -INFINITY;
+        int be = INT_MAX;
+#pragma unroll
+        for (int s = 0; s < MAXS; ++s) {
+            const int e = lane + 64 * s;
+            if (!((taken >> s) & 1u) && (v[s] > bv || (v[s] == bv && e < be))) {
+                bv = v[s];
+                be = e;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const float ov = __shfl_xor(bv, off, 64);
+            const int oe = __shfl_xor(be, off, 64);
+            if (ov > bv || (ov == bv && oe < be)) {
+                bv = ov;
+                be = oe;
+            }
+        }
+        if ((be & 63) == lane)
+            taken |= 1u << (be >> 6);
+        if (lane == j) {
+            my_v = bv;
+            my_e = be;
+        }
+    }
+    const float m0 = __shfl(my_v, 0, 64);
+    const float ex = lane < k ? expf(my_v - m0) : 0.f;
+    float denom;
+    if (renorm) {
+        denom = wave_sum(ex);
+    } else {
+        float s = 0.f;
+#pragma unroll
+        for (int q = 0; q < MAXS; ++q)
+            if (lane + 64 * q < E)
+                s += expf(v[q] - m0);
+        denom = wave_sum(s);
+    }
+    if (lane < k) {
+        idx_out[lane] = my_e;
+        gate_out[lane] = ex / denom;
+        if (sidx)
+            sidx[lane] = my_e;
+    }
+}
+
+template <int MAXS>
+__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, int T, int E, int k,
+                                              int renorm, int32_t *__restrict__ idx,
+                                              float *__restrict__ gate)
+{
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T)
+        return;
+    topk_wave<MAXS>(logits + (size_t)t * E, E, k, renorm, threadIdx.x & 63, idx + (size_t)t * k,
+                    gate + (size_t)t * k, nullptr);
+}
+
+// ---------------------------------------------------------------------------------
+// Scans and peer matching.
+
+// Exclusive scan of v over the block (blockDim multiple of 64, <= 1024).
+// sh: >= 17 ints of LDS.  *total receives the block sum.
+__device__ int block_excl_scan(int v, int *sh, int *total)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off)
+            x += y;
+    }
+    if (lane == 63)
+        sh[w] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int i = 0; i < nw; ++i) {
+            const int t = sh[i];
+            sh[i] = run;
+            run += t;
+        }
+        sh[16] = run;
+    }
+    __syncthreads();
+    const int res = sh[w] + x - v;
+    *total = sh[16];
+    __syncthreads();
+    return res;
+}
+
+// Lanes of the wave whose key equals this lane's key (valid lanes only).
+__device__ __forceinline__ uint64_t match_peers(int key, bool valid, int nbits)
+{
+    uint64_t m = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (key >> b) & 1;
+        const uint64_t bb = __ballot(valid && bit);
+        m &= bit ? bb : ~bb;
+    }
+    return valid ? m : 0ull;
+}
+
+// Rank the rows [beg, end) in order, one 64-row chunk at a time, against the
+// running per-expert bases in LDS (base[e] = next free position of expert e).
+__device__ __forceinline__ void stable_scatter_wave(const int *__restrict__ keys_lds,
+                                                    const int32_t *__restrict__ keys_g, int beg,
+                                                    int end, int *base, int nbits, int lane,
+                                                    int32_t *__restrict__ perm,
+                                                    int32_t *__restrict__ pos)
+{
+    for (int c0 = beg; c0 < end; c0 += 64) {
+        const int f = c0 + lane;
+        const bool valid = f < end;
+        const int key = valid ? (keys_lds ? keys_lds[f] : keys_g[f]) : 0;
+        const uint64_t peers = match_peers(key, valid, nbits);
+        if (valid) {
+            const int rank = __popcll(peers & lanemask_lt(lane));
+            const int b = base[key];
+            const int p = b + rank;
+            perm[p] = f;
+            pos[f] = p;
+            if (lane == __ffsll((unsigned long long)peers) - 1)
+                base[key] = b + __popcll(peers);
+        }
+    }
+}
+
+__device__ __forceinline__ int key_bits(int E)
+{
+    int b = 0;
+    while ((1 << b) < E)
+        ++b;
+    return b;
+}
+
+// ---------------------------------------------------------------------------------
+// Single-block routing for small R (decode): top-k, counts, scan, active list,
+// prefill tile list and the stable scatter, in one launch.
+template <int MAXS>
+__global__ __launch_bounds__(1024) void k_route_small(
+    const float *__restrict__ logits, int T, int E, int k, int renorm, int MT,
+    int32_t *__restrict__ idx, float *__restrict__ gate, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ perm, int32_t *__restrict__ pos,
+    int32_t *__restrict__ active, int32_t *__restrict__ n_active, int32_t *__restrict__ tiles,
+    int32_t *__restrict__ n_tiles)
+{
+    extern __shared__ int smem[];
+    const int R = T * k;
+    int *sidx = smem;
+    int *hist = smem + R;
+    int *sc = hist + E;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    for (int t = wv; t < T; t += 16)
+        topk_wave<MAXS>(logits + (size_t)t * E, E, k, renorm, lane, idx + (size_t)t * k,
+                        gate + (size_t)t * k, sidx + t * k);
+    for (int e = tid; e < E; e += 1024)
+        hist[e] = 0;
+    __syncthreads();
+    for (int f = tid; f < R; f += 1024)
+        atomicAdd(&hist[sidx[f]], 1);
+    __syncthreads();
+    const int c = tid < E ? hist[tid] : 0;
+    int tot, na, ntt;
+    const int off = block_excl_scan(c, sc, &tot);
+    const int aoff = block_excl_scan(c > 0 ? 1 : 0, sc, &na);
+    const int nte = (c + MT - 1) / MT;
+    const int toff = block_excl_scan(nte, sc, &ntt);
+    if (tid < E) {
+        counts[tid] = c;
+        offsets[tid] = off;
+        if (c > 0)
+            active[aoff] = tid;
+        for (int m = 0; m < nte; ++m) {
+            tiles[2 * (toff + m)] = tid;
+            tiles[2 * (toff + m) + 1] = m * MT;
+        }
+    }
+    if (tid == 0) {
+        offsets[E] = tot;
+        *n_active = na;
+        *n_tiles = ntt;
+    }
+    __syncthreads();
+    if (tid < E)
+        hist[tid] = off;
+    __syncthreads();
+    if (wv == 0)
+        stable_scatter_wave(sidx, nullptr, 0, R, hist, key_bits(E), lane, perm, pos);
+}
+
+// ---------------------------------------------------------------------------------
+// Multi-block counting sort for large R: per-segment counts, one scan block,
+// per-segment stable scatter.  Segment s = rows [s*kSortSeg, (s+1)*kSortSeg).
+
+__global__ __launch_bounds__(256) void k_sort_count(const int32_t *__restrict__ idx, int R, int E,
+                                                    int32_t *__restrict__ seg_counts)
+{
+    extern __shared__ int hist[];
+    for (int e = threadIdx.x; e < E; e += 256)
+        hist[e] = 0;
+    __syncthreads();
+    const int beg = blockIdx.x * kSortSeg, end = min(R, beg + kSortSeg);
+    for (int f = beg + threadIdx.x; f < end; f += 256)
+        atomicAdd(&hist[idx[f]], 1);
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256)
+        seg_counts[(size_t)blockIdx.x * E + e] = hist[e];
+}
+
+__global__ __launch_bounds__(1024) void k_sort_scan(
+    const int32_t *__restrict__ seg_counts, int S, int E, int MT, int32_t *__restrict__ seg_base,
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ active,
+    int32_t *__restrict__ n_active, int32_t *__restrict__ tiles, int32_t *__restrict__ n_tiles)
+{
+    __shared__ int sc[17];
+    const int e = threadIdx.x;
+    int c = 0;
+    if (e < E)
+        for (int s = 0; s < S; ++s) {
+            const int v = seg_counts[(size_t)s * E + e];
+            seg_base[(size_t)s * E + e] = c;
+            c += v;
+        }
+    int tot, na, ntt;
+    const int off = block_excl_scan(c, sc, &tot);
+    const int aoff = block_excl_scan(c > 0 ? 1 : 0, sc, &na);
+    const int nte = (c + MT - 1) / MT;
+    const int toff = block_excl_scan(nte, sc, &ntt);
+    if (e < E) {
+        counts[e] = c;
+        offsets[e] = off;
+        for (int s = 0; s < S; ++s)
+            seg_base[(size_t)s * E + e] += off;
+        if (c > 0)
+            active[aoff] = e;
+        for (int m = 0; m < nte; ++m) {
+            tiles[2 * (toff + m)] = e;
+            tiles[2 * (toff + m) + 1] = m * MT;
+        }
+    }
+    if (e == 0) {
+        offsets[E] = tot;
+        *n_active = na;
+        *n_tiles = ntt;
+    }
+}
+
+// Each of the 4 waves owns a contiguous quarter of the segment; its bases are
+// the segment base plus the counts of the quarters before it.
+__global__ __launch_bounds__(256) void k_sort_scatter(const int32_t *__restrict__ idx, int R, int E,
+                                                      const int32_t *__restrict__ seg_base,
+                                                      int32_t *__restrict__ perm,
+                                                      int32_t *__restrict__ pos)
+{
+    extern __shared__ int hw[];  // [4][E]
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int beg = blockIdx.x * kSortSeg, end = min(R, beg + kSortSeg);
+    constexpr int Q = kSortSeg / 4;
+    const int qb = min(end, beg + w * Q), qe = min(end, beg + (w + 1) * Q);
+    for (int i = threadIdx.x; i < 4 * E; i += 256)
+        hw[i] = 0;
+    __syncthreads();
+    for (int f = qb + lane; f < qe; f += 64)
+        atomicAdd(&hw[w * E + idx[f]], 1);
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) {
+        int run = seg_base[(size_t)blockIdx.x * E + e];
+        for (int q = 0; q < 4; ++q) {
+            const int t = hw[q * E + e];
+            hw[q * E + e] = run;
+            run += t;
+        }
+    }
+    __syncthreads();
+    stable_scatter_wave(nullptr, idx, qb, qe, hw + w * E, key_bits(E), lane, perm, pos);
+}
+
+// ---------------------------------------------------------------------------------
+// Launchers.
+
+int launch_router_logits(const ecf_shape &s, const void *x, const void *wr, int T, float *logits,
+                         hipStream_t st)
+{
+    if (T <= 0)
+        return ECF_OK;
+    ProfScope p("router_logits", st);
+    constexpr int TT = 8;
+    dim3 grid(s.n_experts, (T + TT - 1) / TT);
+    if (s.a_dtype == ECF_BF16)
+        hipLaunchKernelGGL((k_router_logits<true, TT>), grid, dim3(256), 0, st, x, wr, T, s.hidden,
+                           s.n_experts, logits);
+    else
+        hipLaunchKernelGGL((k_router_logits<false, TT>), grid, dim3(256), 0, st, x, wr, T, s.hidden,
+                           s.n_experts, logits);
+    ECF_HIP_CHECK(hipGetLastError());
+    return ECF_OK;
+}
+
+int launch_route(const ecf_shape &s, const float *logits, int T, const RouteOut &o, hipStream_t st)
+{
+    const int E = s.n_experts, k = s.top_k, R = T * k;
+    const int maxs = (E + 63) / 64;
+    if (R <= kSmallRouteRows) {
+        ProfScope p("route_small", st);
+        const size_t sh = sizeof(int) * (size_t)(R + E + 17);
+#define ECF_ROUTE_SMALL(MS)                                                                       \
+    hipLaunchKernelGGL((k_route_small<MS>), dim3(1), dim3(1024), sh, st, logits, T, E, k,         \
+                       s.renorm_topk, kPrefillMT, o.idx, o.gate, o.counts, o.offsets, o.perm,      \
+                       o.pos, o.active, o.n_active, o.tiles, o.n_tiles)
+        if (maxs <= 1)
+            ECF_ROUTE_SMALL(1);
+        else if (maxs <= 2)
+            ECF_ROUTE_SMALL(2);
+        else if (maxs <= 4)
+            ECF_ROUTE_SMALL(4);
+        else if (maxs <= 8)
+            ECF_ROUTE_SMALL(8);
+        else
+            ECF_ROUTE_SMALL(16);
+#undef ECF_ROUTE_SMALL
+        ECF_HIP_CHECK(hipGetLastError());
+        return ECF_OK;
+    }
+    {
+        ProfScope p("topk", st);
+        dim3 grid((T + 3) / 4);
+#define ECF_TOPK(MS)                                                                              \
+    hipLaunchKernelGGL((k_topk<MS>), grid, dim3(256), 0, st, logits, T, E, k, s.renorm_topk, o.idx, \
+                       o.gate)
+        if (maxs <= 1)
+            ECF_TOPK(1);
+        else if (maxs <= 2)
+            ECF_TOPK(2);
+        else if (maxs <= 4)
+            ECF_TOPK(4);
+        else if (maxs <= 8)
+            ECF_TOPK(8);
+        else
+            ECF_TOPK(16);
+#undef ECF_TOPK
+        ECF_HIP_CHECK(hipGetLastError());
+    }
+    const int S = (R + kSortSeg - 1) / kSortSeg;
+    {
+        ProfScope p("sort_count", st);
+        hipLaunchKernelGGL(k_sort_count, dim3(S), dim3(256), sizeof(int) * E, st, o.idx, R, E,
+                           o.seg_counts);
+        ECF_HIP_CHECK(hipGetLastError());
+    }
+    {
+        ProfScope p("sort_scan", st);
+        hipLaunchKernelGGL(k_sort_scan, dim3(1), dim3(1024), 0, st, o.seg_counts, S, E, kPrefillMT,
+                           o.seg_base, o.counts, o.offsets, o.active, o.n_active, o.tiles,
+                           o.n_tiles);
+        ECF_HIP_CHECK(hipGetLastError());
+    }
+    {
+        ProfScope p("sort_scatter", st);
+        hipLaunchKernelGGL(k_sort_scatter, dim3(S), dim3(256), sizeof(int) * 4 * E, st, o.idx, R, E,
+                           o.seg_base, o.perm, o.pos);
+        ECF_HIP_CHECK(hipGetLastError());
+    }
+    return ECF_OK;
+}
+
+}  // namespace ecf

@@ -1,0 +1,260 @@
+/*
+ * ecf.h -- C ABI of libecf, one expert-cached Mixture-of-Experts layer on an
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer: router softmax/top-k, token->expert permutation, SwiGLU expert
+ * FFNs (fp32, bf16 or MXFP4 weights) and the gate-weighted combine.  Experts
+ * either all sit in device memory, or live in a pinned host pool (the source
+ * of truth) with a fixed pool of device slots in front of it, one LRU shared
+ * by all layers.  On a miss, the bandwidth-adaptive q* split copies about
+ * m * B_P / B_H of the m missed experts into slots and computes the rest on
+ * host cores; the two partial sums are added.
+ *
+ * Sources (page title, section), quoted nowhere, restated here:
+ *  [TF]  techfeed summary of "Meet FreeToken: An Edge-Native MoE Serving
+ *        Engine ..." (MarkTechPost), section "FreeToken's three core
+ *        mechanisms": "Bandwidth-adaptive execution (q* policy)" and
+ *        "Semantic-aware caching".
+ *  [PL]  FreeToken paper explainer (ta-paperlens), sections "Design: two-tier
+ *        expert memory" and "Prefill: full-layer double buffer and semantic
+ *        anchors".
+ *  [LE]  leadeas blog on FreeToken, section "Using VRAM as a cache --
+ *        bandwidth-adaptive CPU-GPU co-execution".
+ *
+ * Conventions for every call:
+ *  - Pointers prefixed d_ are device memory, h_ are host memory.  Every
+ *    buffer is owned by the caller; the library keeps no pointer beyond a
+ *    call except the slot base inside an ecf_cache and the host pool table
+ *    the caller hands to ecf_cache_create.
+ *  - Streams and events are hipStream_t / hipEvent_t passed as void*.
+ *    NULL means the default stream.
+ *  - Return value: ECF_OK (0) or a negative ECF_* code; the thread-local
+ *    ecf_last_error() explains the last failure.  No C++ exception crosses
+ *    the ABI.  Kernel faults are asynchronous and surface at the next
+ *    synchronising call as ECF_EHIP.
+ *  - The library never allocates device memory on a forward call; it uses
+ *    the caller's workspace.  A cache owns a small pinned host staging area
+ *    and a host thread pool, both allocated once at ecf_cache_create.
+ */
+#ifndef ECF_H
+#define ECF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ----------------------------------------------------------- */
+#define ECF_OK 0
+#define ECF_EINVAL (-1)       /* bad argument (shape, NULL, out of range) */
+#define ECF_ENOSPC (-2)       /* not enough cache slots / buffer too small */
+#define ECF_EHIP (-3)         /* a HIP runtime call failed */
+#define ECF_EUNSUPPORTED (-4) /* valid but not implemented combination */
+#define ECF_ESTATE (-5)       /* call out of order (e.g. evict without lookup) */
+
+/* Message for the last failure on the calling thread ("" if none). */
+const char *ecf_last_error(void);
+
+/* ---- shapes and expert blobs ------------------------------------------------- */
+typedef enum { ECF_F32 = 0, ECF_BF16 = 1, ECF_MXFP4 = 2 } ecf_dtype;
+
+typedef struct {
+    int32_t hidden;      /* d: model width; multiple of 64 (of 128 for MXFP4 or the
+                            prefill path) */
+    int32_t inter;       /* I: expert intermediate width; multiple of 64 */
+    int32_t n_experts;   /* E: routed experts per layer, 1..1024 */
+    int32_t top_k;       /* k: experts per token, 1..min(E, 32) */
+    int32_t w_dtype;     /* expert weight encoding, ecf_dtype */
+    int32_t a_dtype;     /* activation and router-weight encoding: ECF_F32 or ECF_BF16
+                            (must be ECF_BF16 for ECF_BF16 / ECF_MXFP4 weights) */
+    int32_t renorm_topk; /* 1: gates = softmax over the k selected logits;
+                            0: gates = full softmax over E, read at the selected */
+} ecf_shape;
+
+/*
+ * One expert slot blob holds every tensor needed to evaluate one (layer,
+ * expert) pair [PL "Design: two-tier expert memory"], each section starting
+ * at a 256-byte boundary:
+ *   W_gate [I][d], W_up [I][d], W_down [d][I]   (row-major, reduction dim contiguous)
+ * and, for ECF_MXFP4, the E8M0 scales S_gate [I][d/32], S_up [I][d/32],
+ * S_down [d][I/32].  MXFP4 element 2i is the low nibble of byte i (OCP MX v1.0
+ * E2M1); 32 consecutive elements along the reduction dim share one scale.
+ * ecf_expert_layout writes the byte offsets of the six sections (the last
+ * three are 0 for non-MXFP4).
+ */
+size_t ecf_expert_bytes(const ecf_shape *shape);
+int ecf_expert_layout(const ecf_shape *shape, size_t offsets_out[6]);
+
+/* Device workspace bytes a forward call needs for up to max_tokens tokens. */
+size_t ecf_workspace_bytes(const ecf_shape *shape, int32_t max_tokens);
+
+/* ---- q* split [TF "Bandwidth-adaptive execution (q* policy)"] ----------------
+ * PCIe copies and CPU expert execution read the same host memory: with PCIe
+ * drawing b_p of the host bandwidth b_h, the CPU has b_h - b_p left.  Of m
+ * missed experts, copying q takes q/b_p and computing m-q on the CPU takes
+ * (m-q)/(b_h-b_p) (per expert size); the real balance is q = m*b_p/b_h.
+ * Returns the integer q in [0, m] with the smaller of the two makespans at
+ * floor/ceil of m*b_p/b_h (equal makespans, within relative 1e-12, take the
+ * larger q).  b_p <= 0 -> 0; b_p >= b_h -> m.  Returns ECF_EINVAL (< 0) for
+ * m < 0, b_h <= 0 or NaN arguments.  Pure function, thread-safe.
+ */
+int32_t qstar_split(int32_t m, double b_p, double b_h);
+
+/* ---- the shared expert cache [TF "Semantic-aware caching"; PL "Design: two-tier
+ *      expert memory"] -------------------------------------------------------------
+ * Host-side metadata of one LRU over (layer, expert) pairs, shared by all
+ * layers, in front of n_slots device slots of slot_bytes each, at
+ * d_slots + slot * slot_bytes (caller-owned, room for max_slots slots).
+ * h_pool[layer * n_experts + expert] is the pinned host blob of that pair
+ * (the source of truth; entries may alias), or h_pool may be NULL if the
+ * caller never asks the library to copy or host-compute experts.
+ * host_threads sizes the pool of CPU threads that evaluate host-assigned
+ * experts (0 = all hardware threads).  A cache is not thread-safe: one
+ * caller thread per cache.
+ */
+typedef struct ecf_cache ecf_cache;
+
+typedef struct {
+    int64_t lookups, hits, misses, inserts, evictions, dropped;
+} ecf_cache_stats;
+
+int ecf_cache_create(int32_t n_layers, int32_t n_experts, int32_t n_slots, int32_t max_slots,
+                     size_t slot_bytes, void *d_slots, const void *const *h_pool,
+                     int32_t host_threads, ecf_cache **out);
+void ecf_cache_destroy(ecf_cache *cache);
+
+/*
+ * Start a layer-step of `layer` and look up experts[0..n) (distinct, in the
+ * order the caller wants them touched; the forward call uses ascending id).
+ * slots[i] = the resident slot, or -1 on a miss.  Hits become most recently
+ * used, in the given order, and are pinned for the rest of this layer-step.
+ */
+int expert_cache_lookup(ecf_cache *cache, int32_t layer, const int32_t *experts, int32_t n,
+                        int32_t *slots);
+
+/*
+ * Bind experts[0..n) (missed, distinct) of the current layer-step's layer to
+ * slots: the lowest free slot, else the least recently used entry not pinned
+ * by this layer-step (which is evicted).  slots[i] receives the slot;
+ * victims (nullable) receives the evicted pair as layer * n_experts + expert,
+ * or -1 when a free slot was used.  New entries become most recently used and
+ * are pinned.  The caller must then copy the experts' blobs into their slots
+ * before any kernel reads them.  ECF_ENOSPC, with no change made, if fewer
+ * than n slots can be had; ECF_ESTATE if no layer-step is open or `layer`
+ * differs from it; ECF_EINVAL if an expert is already resident.
+ */
+int expert_cache_evict(ecf_cache *cache, int32_t layer, const int32_t *experts, int32_t n,
+                       int32_t *slots, int32_t *victims);
+
+/* Slots a bind in the current layer-step could still take (free + unpinned). */
+int32_t ecf_cache_available(const ecf_cache *cache);
+/* Resident slot of (layer, expert) or -1; does not touch the LRU order. */
+int32_t ecf_cache_slot_of(const ecf_cache *cache, int32_t layer, int32_t expert);
+int ecf_cache_get_stats(const ecf_cache *cache, ecf_cache_stats *out);
+
+/*
+ * Elastic resize at a safe point (between forward calls) [PL "Design: two-tier
+ * expert memory": the host pool stays the source of truth, so the cache may
+ * shrink or grow at any time without changing results].  Entries in slots
+ * >= n_slots are dropped; growing adds free slots, up to max_slots.
+ */
+int ecf_cache_resize(ecf_cache *cache, int32_t n_slots);
+
+/* ---- prefill layer prefetch [PL "Prefill: full-layer double buffer ..."] ------
+ * Queue one copy of a whole layer's expert blobs (bytes, contiguous, pinned
+ * host) into d_buf on copy_stream, then record done_event (nullable) on it.
+ * The copy does not depend on routing, so it may start before the layer's
+ * router has run.  Asynchronous; returns once queued.  ECF_ENOSPC if
+ * buf_capacity < bytes (the caller then falls back to on-demand copies).
+ */
+int prefetch_layer(const void *h_layer_blob, void *d_buf, size_t bytes, size_t buf_capacity,
+                   void *copy_stream, void *done_event);
+
+/* ---- one layer forward --------------------------------------------------------- */
+enum { ECF_Q_AUTO = 0, ECF_Q_ALL_GPU = 1, ECF_Q_ALL_HOST = 2, ECF_Q_FIXED = 3 };
+enum { ECF_PATH_AUTO = 0, ECF_PATH_DECODE = 1, ECF_PATH_PREFILL = 2 };
+
+typedef struct {
+    int32_t n_unique;  /* experts routed to by at least one token */
+    int32_t hits;      /* of those, resident in a slot */
+    int32_t misses;    /* m */
+    int32_t q;         /* misses copied into slots */
+    int32_t host;      /* misses computed on the host (m - q) */
+    int32_t path;      /* ECF_PATH_DECODE or ECF_PATH_PREFILL */
+    int64_t bytes_h2d;  /* expert bytes copied host->device */
+    int64_t bytes_host; /* expert bytes read by host threads */
+    double ms_wait_route; /* host time blocked on the routing readback */
+    double ms_host_ffn;   /* host time spent in host experts */
+} ecf_step_stats;
+
+typedef struct {
+    ecf_shape shape;
+    int32_t layer;               /* layer id (cache key) */
+    /* routing input: exactly one of the two */
+    const void *d_router_w;      /* [E][d] in a_dtype: logits = x . W_r^T in fp64, rounded to fp32 */
+    const float *d_router_logits;/* [T][E] fp32, given directly */
+    /* expert placement: exactly one of the two */
+    const uint64_t *d_expert_ptrs; /* [E] device addresses of resident blobs (all experts resident) */
+    ecf_cache *cache;              /* expert cache (blobs from the cache's host pool) */
+    /* q* policy (cache mode) */
+    double b_p, b_h;             /* bandwidth figures for qstar_split (any unit, same for both) */
+    int32_t q_mode;              /* ECF_Q_*: AUTO uses qstar_split; the others are for tests */
+    int32_t q_fixed;             /* q for ECF_Q_FIXED (clamped to [0, m]) */
+    int32_t path;                /* ECF_PATH_*: AUTO picks by rows per expert and dtype */
+    /* buffers */
+    void *d_ws;                  /* workspace, >= ecf_workspace_bytes(shape, T) bytes, 256-B aligned */
+    size_t ws_bytes;
+    void *stream;                /* compute stream */
+    void *copy_stream;           /* cache mode: stream for slot fills (NULL = stream) */
+    const float *d_residual;     /* optional [T][d] fp32 added to the output (may equal d_out) */
+    void *d_out_act;             /* optional [T][d] copy of the output in a_dtype (next layer input) */
+    /* optional debug outputs (device, nullable) */
+    int32_t *d_topk_idx;         /* [T][k] selected experts, logit descending, ties -> lower id */
+    float *d_topk_gate;          /* [T][k] gates */
+    int32_t *d_counts;           /* [E] rows per expert */
+    int32_t *d_perm;             /* [T*k] row r of the expert-sorted order -> flat (t*k + j) */
+    float *d_logits;             /* [T][E] router logits (router-weight mode only) */
+} ecf_layer_args;
+
+/*
+ * out[t][:] = residual[t][:] + sum_{j=0..k-1} gate[t][j] * FFN_{idx[t][j]}(x[t])
+ * with FFN_e(v) = W_down[e] . (silu(W_gate[e] . v) * (W_up[e] . v)), x [T][d]
+ * in a_dtype, out [T][d] fp32.  All-resident mode is fully asynchronous on
+ * args->stream.  Cache mode blocks the calling thread once on the routing
+ * readback (the q* decision is taken on the host from the step's miss count
+ * [TF "Bandwidth-adaptive execution (q* policy)"]), computes host-assigned
+ * experts on the cache's host threads, and returns with the rest queued.
+ * n_tokens == 0 is a no-op.  stats (nullable) receives the step's figures.
+ */
+int moe_layer_forward(const ecf_layer_args *args, const void *d_x, int32_t n_tokens, float *d_out,
+                      ecf_step_stats *stats);
+
+/*
+ * The host half of the split on its own: y[f][:] = FFN_e(x[f / k]) for the rows
+ * f listed per expert, evaluated by n_threads host threads (0 = default) the
+ * same way a forward call evaluates host-assigned experts [TF "Bandwidth-
+ * adaptive execution (q* policy)": missed experts not copied run on the CPU
+ * straight from host memory].  h_blobs[i] is the host blob of job i (bf16 or
+ * fp32 weights), rows of job i are rows[sum(n_rows[<i]) .. + n_rows[i]];
+ * h_x [T][d] in a_dtype, h_y [T*k][d] fp32 (only listed rows written).  No
+ * GPU is touched.
+ */
+int ecf_host_experts(const ecf_shape *shape, int32_t n_jobs, const void *const *h_blobs,
+                     const int32_t *n_rows, const int32_t *rows, const void *h_x, int32_t n_tokens,
+                     float *h_y, int32_t n_threads);
+
+/* ---- measurement hooks ------------------------------------------------------------- */
+/* When enabled, every kernel launch is bracketed by HIP events on its stream
+ * and its duration is accumulated per kernel name (adds event overhead). */
+int ecf_profile_enable(int32_t on);
+/* Kernel name i (0-based) with its launch count and summed milliseconds;
+ * ECF_EINVAL when i is past the last name.  Synchronises the device. */
+int ecf_profile_get(int32_t i, const char **name, int64_t *launches, double *total_ms);
+int ecf_profile_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ECF_H */

@@ -1,0 +1,124 @@
+"""Helpers shared by the GPU parity tests: build a layer's inputs once (seeded,
+from ecf_synth), run libecf through the C ABI, run the oracle on the same
+bytes, and compare."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import ecf_synth as syn
+import expert_cache_ffn_amd as ecf
+import oracle
+from expert_cache_ffn_amd.layer import ExpertPool, Layer
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def shape_of(cfg, renorm=1):
+    return ecf.make_shape(cfg.hidden, cfg.inter, cfg.experts, cfg.top_k, cfg.w_dtype, cfg.a_dtype, renorm)
+
+
+class Case:
+    """Experts (device pool + lazily copied host tensors), router input, x."""
+
+    def __init__(self, cfg, T, layer=0, batch=0, gen_device="cpu", renorm=1, logits=None):
+        self.cfg, self.T = cfg, T
+        self.shape = shape_of(cfg, renorm)
+        self.renorm = renorm
+        self.gen_device = gen_device
+        self.pool = ExpertPool(self.shape, "cuda")
+        self.host_experts = {}
+        for e in range(cfg.experts):
+            ex = syn.expert_weights(cfg, layer, e, device=gen_device)
+            self.pool.load(e, {k: v.to("cuda") for k, v in ex.items()})
+            if gen_device == "cpu":
+                self.host_experts[e] = ex
+        self.layer_id = layer
+        self.x = syn.activations(cfg, T, layer=layer, batch=batch, device=gen_device)
+        self.router_w = None
+        if logits is not None:
+            self.logits = logits.to(gen_device)
+        elif cfg.logits == "router":
+            self.router_w = syn.router_weights(cfg, layer, device=gen_device)
+            self.logits = None
+        else:
+            self.logits = syn.router_logits(cfg, T, layer=layer, step=batch, device=gen_device)
+
+    def host_expert(self, e):
+        if e not in self.host_experts:
+            ex = {k: v.detach().cpu() for k, v in syn.expert_weights(self.cfg, self.layer_id, e,
+                                                                       device="cuda").items()}
+            self.host_experts[e] = ex
+        return self.host_experts[e]
+
+    def run(self, path=ecf.ECF_PATH_AUTO, residual=None, want_logits=True, layer=None):
+        T, k, E = self.T, self.cfg.top_k, self.cfg.experts
+        L = Layer(self.shape, max(T, 1))
+        dev = lambda t: None if t is None else t.to("cuda").contiguous()
+        x = dev(self.x)
+        out = torch.full((T, self.cfg.hidden), float("nan"), dtype=torch.float32, device="cuda")
+        idx = torch.full((max(T * k, 1),), -7, dtype=torch.int32, device="cuda")
+        gate = torch.zeros(max(T * k, 1), dtype=torch.float32, device="cuda")
+        counts = torch.zeros(E, dtype=torch.int32, device="cuda")
+        perm = torch.full((max(T * k, 1),), -7, dtype=torch.int32, device="cuda")
+        lg_out = torch.zeros((max(T, 1), E), dtype=torch.float32, device="cuda") if self.router_w is not None else None
+        a = L.args(router_w=dev(self.router_w), router_logits=dev(self.logits), expert_ptrs=self.pool.ptrs,
+                   path=path, residual=residual, topk_idx=idx, topk_gate=gate, counts=counts, perm=perm,
+                   logits_out=lg_out)
+        st = L.forward(a, x, out)
+        torch.cuda.synchronize()
+        res = dict(out=out.cpu().numpy(), idx=idx.cpu().numpy()[:T * k].reshape(T, k),
+                   gate=gate.cpu().numpy()[:T * k].reshape(T, k), counts=counts.cpu().numpy(),
+                   perm=perm.cpu().numpy()[:T * k], stats=st)
+        if lg_out is not None:
+            res["logits"] = lg_out.cpu().numpy()[:T]
+        return res
+
+    def oracle(self, tokens=None):
+        """Oracle routing for every token and outputs for `tokens` (default all)."""
+        x = self.x.detach().cpu()
+        if self.logits is not None:
+            lg = self.logits.detach().cpu().numpy()
+        else:
+            lg = oracle.logits(x, self.router_w.detach().cpu())
+        idx, g = oracle.route(lg, self.cfg.top_k, bool(self.renorm))
+        counts, offsets, perm, pos = oracle.permute(idx, self.cfg.experts)
+        toks = np.arange(self.T) if tokens is None else np.asarray(tokens)
+        need = sorted(set(int(e) for e in idx[toks].ravel()))
+        experts = [None] * self.cfg.experts
+        for e in need:
+            experts[e] = self.host_expert(e)
+        out = oracle.moe_tokens(x, experts, idx, g, toks, self.cfg.w_dtype) if len(toks) else np.zeros((0, self.cfg.hidden))
+        return dict(logits=lg, idx=idx, gates=g, counts=counts, perm=perm, out=out, tokens=toks)
+
+
+def compare(res, ref, tol_rel, label=""):
+    """Routing bit-exact (where logits agree), gates close, outputs within
+    tol_rel * RMS(oracle output).  Returns the measured max error / RMS."""
+    T = res["idx"].shape[0]
+    same_rows = np.ones(T, bool)
+    if "logits" in res:
+        gl, ol = res["logits"], ref["logits"]
+        ulp = np.spacing(np.abs(ol).astype(np.float32))
+        assert np.all(np.abs(gl - ol) <= ulp), f"{label}: router logits beyond 1 ulp"
+        same_rows = np.all(gl == ol, axis=1)
+        if not same_rows.all():
+            say(f"{label}: {np.sum(~same_rows)} token(s) with 1-ulp logit differences")
+    assert np.array_equal(res["idx"][same_rows], ref["idx"][same_rows]), f"{label}: top-k indices differ"
+    assert np.allclose(res["gate"], ref["gates"], rtol=2e-6, atol=1e-7), f"{label}: gates differ"
+    if same_rows.all():
+        assert np.array_equal(res["counts"], ref["counts"]), f"{label}: counts differ"
+        assert np.array_equal(res["perm"], ref["perm"]), f"{label}: permutation differs"
+    got = res["out"][ref["tokens"]]
+    want = ref["out"]
+    rms = float(np.sqrt(np.mean(want ** 2))) if want.size else 1.0
+    err = float(np.max(np.abs(got - want))) / rms if want.size else 0.0
+    say(f"{label}: max|err|/RMS = {err:.3e} (tolerance {tol_rel:g}), RMS = {rms:.4g}")
+    assert np.all(np.isfinite(got)), f"{label}: non-finite output"
+    assert err <= tol_rel, f"{label}: max|err|/RMS {err:.3e} > {tol_rel}"
+    return err

@@ -1,0 +1,173 @@
+"""GPU parity: libecf (through the C ABI) against the oracle on the same seeded
+inputs.  Routing, counts and the permutation must match bit-exactly; outputs
+within max|err| <= tol * RMS(oracle output): 1e-4 for fp32 weights, 2e-2 for
+bf16, 5e-2 for MXFP4."""
+import numpy as np
+import pytest
+import torch
+
+import ecf_synth as syn
+import expert_cache_ffn_amd as ecf
+from gpu_util import Case, compare, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2, "mxfp4": 5e-2}
+
+
+def cfg_small(**kw):
+    base = dict(cid=50, name="small", tokens=(8,), hidden=512, experts=8, inter=256, top_k=2,
+                w_dtype="bf16", a_dtype="bf16", logits="router")
+    base.update(kw)
+    return syn.gen.Config(**base)
+
+
+# ---- tiny fp32 layer (64 tokens, d 256, 16 experts, I 128, top-2) ---------------------
+
+def test_tiny_fp32_layer():
+    cfg = syn.CONFIGS["tiny"]
+    say("case: tiny fp32 T=64")
+    c = Case(cfg, 64)
+    res = c.run()
+    assert res["stats"]["path"] == ecf.ECF_PATH_DECODE
+    compare(res, c.oracle(), TOL["f32"], "tiny")
+
+
+# ---- decode bf16 at full size (d 4096, 256 experts, I 1024, top-6) ----------------------
+
+@pytest.fixture(scope="module")
+def decode_cases():
+    cfg = syn.CONFIGS["decode"]
+    return cfg
+
+
+@pytest.mark.parametrize("T", [1, 4, 16])
+def test_decode_bf16_full_size(decode_cases, T):
+    cfg = decode_cases
+    say(f"case: decode bf16 full size T={T}")
+    c = Case(cfg, T, gen_device="cuda")
+    res = c.run()
+    assert res["stats"]["path"] == ecf.ECF_PATH_DECODE
+    compare(res, c.oracle(), TOL["bf16"], f"decode T={T}")
+    del c
+    torch.cuda.empty_cache()
+
+
+# ---- edge cases on small shapes -------------------------------------------------------
+
+@pytest.mark.parametrize("path", [ecf.ECF_PATH_DECODE, ecf.ECF_PATH_PREFILL])
+@pytest.mark.parametrize("E,k,T", [(1, 1, 5), (8, 8, 3), (8, 2, 1), (16, 4, 37)])
+def test_small_shapes_both_paths(path, E, k, T):
+    cfg = cfg_small(experts=E, top_k=k, cid=51 + E)
+    say(f"case: small E={E} k={k} T={T} path={path}")
+    c = Case(cfg, T)
+    res = c.run(path=path)
+    assert res["stats"]["path"] == path
+    compare(res, c.oracle(), TOL["bf16"], f"small E={E} k={k} T={T} path={path}")
+
+
+def test_tied_logits_pick_lowest_ids():
+    cfg = cfg_small(logits="uniform", cid=60)
+    T = 5
+    lg = torch.zeros((T, cfg.experts), dtype=torch.float32)
+    lg[:, 5] = 1.0
+    c = Case(cfg, T, logits=lg)
+    res = c.run()
+    assert np.all(res["idx"] == np.array([5, 0])), res["idx"]
+    compare(res, c.oracle(), TOL["bf16"], "ties")
+
+
+def test_no_renorm_gates():
+    cfg = cfg_small(cid=61)
+    c = Case(cfg, 6, renorm=0)
+    res = c.run()
+    compare(res, c.oracle(), TOL["bf16"], "renorm=0")
+    assert np.all(res["gate"].sum(1) < 1.0)
+
+
+def test_zero_tokens_is_noop():
+    cfg = cfg_small(cid=62)
+    c = Case(cfg, 0)
+    res = c.run()
+    assert res["out"].shape == (0, cfg.hidden)
+    assert res["stats"]["n_unique"] == 0
+
+
+def test_residual_added():
+    cfg = cfg_small(cid=63)
+    c = Case(cfg, 4)
+    base = c.run()
+    r = torch.randn(4, cfg.hidden, dtype=torch.float32, device="cuda")
+    res = c.run(residual=r)
+    assert np.allclose(res["out"], base["out"] + r.cpu().numpy(), rtol=0, atol=1e-6)
+
+
+# ---- prefill bf16 (grouped MFMA GEMM) ---------------------------------------------------
+
+@pytest.mark.parametrize("T,E,k,I", [(300, 8, 2, 256), (1000, 4, 2, 128), (97, 32, 6, 192)])
+def test_prefill_bf16_ragged_tiles(T, E, k, I):
+    cfg = cfg_small(experts=E, top_k=k, inter=I, logits="uniform", cid=70 + E)
+    say(f"case: prefill bf16 T={T} E={E} k={k} I={I}")
+    c = Case(cfg, T)
+    res = c.run(path=ecf.ECF_PATH_PREFILL)
+    compare(res, c.oracle(), TOL["bf16"], f"prefill T={T} E={E}")
+
+
+def test_prefill_bf16_full_size_sampled():
+    cfg = syn.CONFIGS["prefill"]
+    say("case: prefill bf16 full size T=4096 (routing all tokens, outputs on 48 sampled)")
+    c = Case(cfg, 4096, gen_device="cuda")
+    res = c.run()
+    assert res["stats"]["path"] == ecf.ECF_PATH_PREFILL
+    toks = np.random.default_rng(0).choice(4096, 48, replace=False)
+    compare(res, c.oracle(tokens=toks), TOL["bf16"], "prefill full")
+    assert res["counts"].min() > 0  # ~all experts active
+    del c
+    torch.cuda.empty_cache()
+
+
+# ---- prefill MXFP4 ------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,E,k,I", [(260, 8, 2, 256), (64, 4, 4, 128)])
+def test_prefill_mxfp4_small(T, E, k, I):
+    cfg = cfg_small(experts=E, top_k=k, inter=I, w_dtype="mxfp4", logits="normal_t", temperature=0.5,
+                    cid=80 + E)
+    say(f"case: prefill mxfp4 T={T} E={E} k={k}")
+    c = Case(cfg, T)
+    res = c.run()
+    assert res["stats"]["path"] == ecf.ECF_PATH_PREFILL
+    compare(res, c.oracle(), TOL["mxfp4"], f"mxfp4 T={T} E={E}")
+
+
+def test_prefill_mxfp4_full_size_sampled():
+    cfg = syn.CONFIGS["prefill_fp4"]
+    say("case: prefill mxfp4 full size T=8192 (routing all tokens, outputs on 24 sampled)")
+    c = Case(cfg, 8192, gen_device="cuda")
+    res = c.run()
+    toks = np.random.default_rng(1).choice(8192, 24, replace=False)
+    compare(res, c.oracle(tokens=toks), TOL["mxfp4"], "mxfp4 full")
+    del c
+    torch.cuda.empty_cache()
+
+
+# ---- properties ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("path", [ecf.ECF_PATH_DECODE, ecf.ECF_PATH_PREFILL])
+def test_run_to_run_bit_identical(path):
+    cfg = cfg_small(experts=16, top_k=4, cid=90)
+    c = Case(cfg, 48)
+    a = c.run(path=path)
+    for _ in range(3):
+        b = c.run(path=path)
+        assert np.array_equal(a["out"], b["out"])
+        assert np.array_equal(a["perm"], b["perm"])
+
+
+def test_decode_and_prefill_paths_agree():
+    cfg = cfg_small(experts=16, top_k=4, cid=91)
+    c = Case(cfg, 40)
+    a = c.run(path=ecf.ECF_PATH_DECODE)
+    b = c.run(path=ecf.ECF_PATH_PREFILL)
+    rms = np.sqrt(np.mean(a["out"] ** 2))
+    assert np.max(np.abs(a["out"] - b["out"])) <= TOL["bf16"] * rms
+    assert np.array_equal(a["perm"], b["perm"])

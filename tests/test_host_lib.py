@@ -1,0 +1,226 @@
+"""CPU tests of libecf's host side: exports, layouts, q*, the shared LRU and
+the host expert FFN, each against the oracle (no GPU calls)."""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import ecf_synth as syn
+import expert_cache_ffn_amd as ecf
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLD = os.path.join(ROOT, "tests", "golden")
+
+
+def test_library_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "ecf.h")).read()
+    hdr = re.sub(r"/\*.*?\*/", "", hdr, flags=re.S)
+    hdr = "\n".join(l for l in hdr.splitlines() if not l.lstrip().startswith("#"))
+    declared = set(re.findall(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*\([^;{]*\)\s*;", hdr))
+    declared = {n for n in declared if n not in ("if", "while", "sizeof")}
+    assert declared == set(ecf.EXPORTS), declared ^ set(ecf.EXPORTS)
+    L = ecf.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_expert_blob_sizes():
+    bf = ecf.make_shape(4096, 1024, 256, 6, "bf16", "bf16")
+    assert ecf.ecf_expert_bytes(bf) == 6 * 4096 * 1024  # 25,165,824
+    mx = ecf.make_shape(4096, 2048, 256, 8, "mxfp4", "bf16")
+    assert ecf.ecf_expert_bytes(mx) == 13_369_344       # 1.5 d I + 3 d I / 32
+    offs = ecf.ecf_expert_layout(mx)
+    assert offs[:3] == [0, 4096 * 2048 // 2, 2 * 4096 * 2048 // 2]
+    assert all(o % 256 == 0 for o in offs)
+    f32 = ecf.make_shape(256, 128, 16, 2, "f32", "f32")
+    assert ecf.ecf_expert_bytes(f32) == 12 * 256 * 128
+
+
+def test_invalid_shapes_rejected():
+    for bad in [ecf.make_shape(100, 64, 4, 2), ecf.make_shape(256, 60, 4, 2), ecf.make_shape(256, 64, 4, 5),
+                ecf.make_shape(256, 64, 2000, 2), ecf.make_shape(256, 64, 4, 2, "bf16", "f32")]:
+        with pytest.raises(ecf.EcfError):
+            ecf.ecf_expert_bytes(bad)
+    assert ecf.ecf_workspace_bytes(ecf.make_shape(256, 64, 4, 2), 10) > 0
+
+
+# ---- q* -----------------------------------------------------------------------------
+
+def test_qstar_matches_oracle_golden():
+    for line in open(os.path.join(GOLD, "qstar_splits.txt")):
+        if not line.strip() or line.startswith("#"):
+            continue
+        bp, bh, m, q = line.split()
+        assert ecf.qstar_split(int(m), float(bp), float(bh)) == int(q), line
+
+
+def test_qstar_matches_oracle_brute_force():
+    rng = np.random.default_rng(5)
+    for _ in range(4000):
+        bh = float(rng.uniform(0.5, 300))
+        bp = float(rng.choice([rng.uniform(0, 1), 0.4, 0.5, 0.25, 0.75])) * bh
+        m = int(rng.integers(0, 200))
+        assert ecf.qstar_split(m, bp, bh) == oracle.qstar(m, bp, bh), (m, bp, bh)
+    for m in range(0, 64):
+        assert ecf.qstar_split(m, 0.4, 1.0) == oracle.qstar(m, 0.4, 1.0)
+
+
+def test_qstar_errors_and_edges():
+    assert ecf.qstar_split(0, 1, 2) == 0
+    assert ecf.qstar_split(5, 0, 2) == 0
+    assert ecf.qstar_split(5, 2, 2) == 5
+    for bad in [(-1, 1, 2), (3, 1, 0), (3, float("nan"), 1), (3, 1, float("nan"))]:
+        with pytest.raises(ecf.EcfError) as ei:
+            ecf.qstar_split(*bad)
+        assert ei.value.code == ecf.ECF_EINVAL
+
+
+# ---- shared LRU ---------------------------------------------------------------------
+
+FAKE_SLOTS = 1 << 40  # slot memory is never touched by the metadata calls
+
+
+def _run_step(cache, ref, layer, rows, q_of_m):
+    """Drive one layer-step through the C calls the way the forward call does."""
+    U = sorted(rows)
+    slots = ecf.expert_cache_lookup(cache, layer, U)
+    miss = [e for e, s in zip(U, slots) if s < 0]
+    q = min(q_of_m(len(miss)), ecf.ecf_cache_available(cache))
+    order = sorted(miss, key=lambda e: (-rows[e], e))
+    cs, vs = ecf.expert_cache_evict(cache, layer, order[:q]) if q else ([], [])
+    plan = ref.step(layer, rows, q_of_m)
+    assert {e: s for e, s in zip(U, slots) if s >= 0} == plan["hits"]
+    assert dict(zip(order[:q], cs)) == plan["copied"]
+    E = ref.E
+    want_v = {e: (None if v is None else v[0] * E + v[1]) for e, v in plan["victims"].items()}
+    got_v = {e: (None if v < 0 else v) for e, v in zip(order[:q], vs)}
+    assert got_v == want_v
+    assert order[q:] == plan["host"]
+
+
+def test_lru_hand_trace_through_c_api():
+    tr = json.load(open(os.path.join(GOLD, "lru_trace.json")))
+    E = tr["n_experts"]
+    cache = ecf.ecf_cache_create(2, E, tr["n_slots"], tr["n_slots"], 4096, FAKE_SLOTS)
+    try:
+        ref = oracle.LRURef(tr["n_slots"], E)
+        rules = {"all": lambda m: m, "q04": lambda m: ecf.qstar_split(m, 0.4, 1.0)}
+        for st in tr["steps"]:
+            _run_step(cache, ref, st["layer"], {int(e): n for e, n in st["rows"].items()}, rules[st["q"]])
+        s = ecf.ecf_cache_get_stats(cache)
+        assert {k: s[k] for k in tr["stats"]} == tr["stats"]
+    finally:
+        ecf.ecf_cache_destroy(cache)
+
+
+@pytest.mark.parametrize("n_slots,L,E,k,T", [(37, 5, 32, 4, 4), (8, 3, 16, 2, 3), (200, 43, 64, 6, 16)])
+def test_lru_random_trace_against_reference(n_slots, L, E, k, T):
+    rng = np.random.default_rng(n_slots + L)
+    cache = ecf.ecf_cache_create(L, E, n_slots, n_slots, 4096, FAKE_SLOTS)
+    ref = oracle.LRURef(n_slots, E)
+    zipf = 1.0 / np.arange(1, E + 1) ** 1.1
+    zipf /= zipf.sum()
+    rules = [lambda m: m, lambda m: 0, lambda m: ecf.qstar_split(m, 0.4, 1.0),
+             lambda m: ecf.qstar_split(m, 0.68, 1.0)]
+    try:
+        for step in range(300):
+            layer = step % L
+            rows = {}
+            for _ in range(T):
+                for e in rng.choice(E, size=k, replace=False, p=zipf):
+                    rows[int(e)] = rows.get(int(e), 0) + 1
+            _run_step(cache, ref, layer, rows, rules[step % len(rules)])
+        assert {k2: v for k2, v in ecf.ecf_cache_get_stats(cache).items() if k2 != "dropped"} == ref.stats
+        for l in range(L):
+            for e in range(E):
+                s = ref.resident(l, e)
+                assert ecf.ecf_cache_slot_of(cache, l, e) == (-1 if s is None else s)
+    finally:
+        ecf.ecf_cache_destroy(cache)
+
+
+def test_cache_error_paths():
+    cache = ecf.ecf_cache_create(2, 8, 2, 4, 4096, FAKE_SLOTS)
+    try:
+        with pytest.raises(ecf.EcfError) as ei:
+            ecf.expert_cache_evict(cache, 0, [1])      # no layer-step open
+        assert ei.value.code == ecf.ECF_ESTATE
+        ecf.expert_cache_lookup(cache, 0, [1, 2, 3])
+        with pytest.raises(ecf.EcfError) as ei:
+            ecf.expert_cache_evict(cache, 1, [1])      # other layer
+        assert ei.value.code == ecf.ECF_ESTATE
+        with pytest.raises(ecf.EcfError) as ei:
+            ecf.expert_cache_evict(cache, 0, [1, 2, 3])  # 3 wanted, 2 slots
+        assert ei.value.code == ecf.ECF_ENOSPC
+        assert ecf.ecf_cache_get_stats(cache)["inserts"] == 0  # no change on failure
+        assert ecf.expert_cache_evict(cache, 0, [1, 2])[0] == [0, 1]
+        with pytest.raises(ecf.EcfError) as ei:
+            ecf.expert_cache_evict(cache, 0, [1])      # already resident
+        assert ei.value.code == ecf.ECF_EINVAL
+        assert ecf.ecf_cache_available(cache) == 0     # both slots pinned by this step
+        ecf.expert_cache_lookup(cache, 0, [4])         # new step: nothing pinned
+        assert ecf.ecf_cache_available(cache) == 2
+        with pytest.raises(ecf.EcfError):
+            ecf.ecf_cache_resize(cache, 5)             # above max_slots
+        with pytest.raises(ecf.EcfError):
+            ecf.expert_cache_lookup(cache, 2, [0])     # layer out of range
+    finally:
+        ecf.ecf_cache_destroy(cache)
+
+
+def test_cache_resize_matches_reference():
+    cache = ecf.ecf_cache_create(3, 16, 6, 10, 4096, FAKE_SLOTS)
+    ref = oracle.LRURef(6, 16)
+    try:
+        _run_step(cache, ref, 0, {0: 1, 1: 1, 2: 1, 3: 1, 4: 1, 5: 1}, lambda m: m)
+        ecf.ecf_cache_resize(cache, 3)
+        ref.resize(3)
+        assert ecf.ecf_cache_get_stats(cache)["dropped"] == 3
+        for e in range(6):
+            s = ref.resident(0, e)
+            assert ecf.ecf_cache_slot_of(cache, 0, e) == (-1 if s is None else s)
+        ecf.ecf_cache_resize(cache, 10)
+        ref.resize(10)
+        _run_step(cache, ref, 1, {e: 1 for e in range(8)}, lambda m: m)
+        _run_step(cache, ref, 0, {e: 2 for e in range(4, 12)}, lambda m: m)
+    finally:
+        ecf.ecf_cache_destroy(cache)
+
+
+# ---- host expert FFN against the oracle -------------------------------------------------
+
+def _blob(shape, tensors):
+    nbytes = ecf.ecf_expert_bytes(shape)
+    buf = torch.zeros(nbytes, dtype=torch.uint8)
+    from expert_cache_ffn_amd.layer import pack_expert
+    pack_expert(shape, tensors, buf)
+    return buf
+
+
+@pytest.mark.parametrize("w_dtype", ["bf16", "f32"])
+def test_host_experts_against_oracle(w_dtype):
+    a_dtype = "bf16" if w_dtype == "bf16" else "f32"
+    cfg = syn.gen.Config(93, "t", (6,), 512, 4, 192, 2, w_dtype, a_dtype, "router")
+    shape = ecf.make_shape(cfg.hidden, cfg.inter, cfg.experts, cfg.top_k, w_dtype, a_dtype)
+    experts = [syn.expert_weights(cfg, 0, e) for e in range(cfg.experts)]
+    blobs = [_blob(shape, ex) for ex in experts]
+    T, k = 6, cfg.top_k
+    x = syn.activations(cfg, T)
+    lg = syn.gen.normal(syn.key_of(93, 0, 9), T * cfg.experts).view(T, cfg.experts).float()
+    idx, _ = oracle.route(lg, k)
+    rows = [[f for f in range(T * k) if idx.reshape(-1)[f] == e] for e in range(cfg.experts)]
+    y = torch.full((T * k, cfg.hidden), float("nan"), dtype=torch.float32)
+    xc = x.contiguous()
+    ecf.ecf_host_experts(shape, [b.data_ptr() for b in blobs], rows, xc.data_ptr(), T, y.data_ptr(), 3)
+    ref = np.zeros((T * k, cfg.hidden))
+    x64 = xc.double().numpy()
+    for e in range(cfg.experts):
+        for f in rows[e]:
+            ref[f] = oracle.expert_ffn(experts[e], x64[f // k], w_dtype)
+    rms = np.sqrt(np.mean(ref ** 2))
+    assert np.max(np.abs(y.numpy() - ref)) <= 1e-5 * rms
