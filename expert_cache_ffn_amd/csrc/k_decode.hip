@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void k_decode_gateup(
     const uint64_t *__restrict__ ptrs, size_t off_gate, size_t off_up,
     const int32_t *__restrict__ active, const int32_t *__restrict__ n_active,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm,
-    const void *__restrict__ x, int d, int I, int k, float *__restrict__ H)
+    const void *__restrict__ x, int d, int I, int k, int E, int R, int ntp, float *__restrict__ H)
 {
     static_assert(2 * IB * KP == 32, "32 groups of 8 lanes per block");
     extern __shared__ float xs[];  // [min(kDecodeNT, T)][d]; an expert has at most T rows
@@ -94,10 +94,12 @@ __global__ __launch_bounds__(256) void k_decode_gateup(
     if ((int)blockIdx.y >= *n_active)
         return;
     const int e = active[blockIdx.y];
-    const uint64_t blob = ptrs[e];
-    if (!blob)
+    if ((unsigned)e >= (unsigned)E)  // routing metadata is produced on the device; never index past it
         return;
+    const uint64_t blob = ptrs[e];
     const int r0 = offsets[e], ne = offsets[e + 1] - r0;
+    if (!blob || r0 < 0 || ne <= 0 || r0 + ne > R)
+        return;
     const int i0 = blockIdx.x * IB;
     const int tid = threadIdx.x, lane = tid & 63, sub = lane & 7;
     const int g = tid >> 3;  // group 0..31
@@ -106,8 +108,8 @@ __global__ __launch_bounds__(256) void k_decode_gateup(
     const int irow = i0 + (rho % IB);
     const char *wrow = (const char *)blob + sec + (size_t)irow * d * (WBF ? 2 : 4);
     const int Lk = d / KP, kbeg = kap * Lk, kend = kbeg + Lk;
-    for (int tp = 0; tp < ne; tp += kDecodeNT) {
-        const int nt = min(kDecodeNT, ne - tp);
+    for (int tp = 0; tp < ne; tp += ntp) {
+        const int nt = min(ntp, ne - tp);
         for (int q = 0; q < nt; ++q) {
             const size_t t = (size_t)(perm[r0 + tp + q] / k);
             for (int c = tid; c < d; c += 256)
@@ -147,7 +149,7 @@ template <bool WBF, int OB, int KP>
 __global__ __launch_bounds__(256) void k_decode_down(
     const uint64_t *__restrict__ ptrs, size_t off_down, const int32_t *__restrict__ active,
     const int32_t *__restrict__ n_active, const int32_t *__restrict__ offsets,
-    const float *__restrict__ H, int d, int I, float *__restrict__ Y)
+    const float *__restrict__ H, int d, int I, int E, int R, int ntp, float *__restrict__ Y)
 {
     static_assert(OB * KP == 32, "32 groups of 8 lanes per block");
     extern __shared__ float hs[];  // [min(kDecodeNT, T)][I]
@@ -155,18 +157,20 @@ __global__ __launch_bounds__(256) void k_decode_down(
     if ((int)blockIdx.y >= *n_active)
         return;
     const int e = active[blockIdx.y];
-    const uint64_t blob = ptrs[e];
-    if (!blob)
+    if ((unsigned)e >= (unsigned)E)
         return;
+    const uint64_t blob = ptrs[e];
     const int r0 = offsets[e], ne = offsets[e + 1] - r0;
+    if (!blob || r0 < 0 || ne <= 0 || r0 + ne > R)
+        return;
     const int o0 = blockIdx.x * OB;
     const int tid = threadIdx.x, lane = tid & 63, sub = lane & 7;
     const int g = tid >> 3;
     const int rho = g % OB, kap = g / OB;
     const char *wrow = (const char *)blob + off_down + (size_t)(o0 + rho) * I * (WBF ? 2 : 4);
     const int Lk = I / KP, kbeg = kap * Lk, kend = kbeg + Lk;
-    for (int tp = 0; tp < ne; tp += kDecodeNT) {
-        const int nt = min(kDecodeNT, ne - tp);
+    for (int tp = 0; tp < ne; tp += ntp) {
+        const int nt = min(ntp, ne - tp);
         for (int q = 0; q < nt; ++q)
             for (int c = tid; c < I; c += 256)
                 hs[q * I + c] = H[(size_t)(r0 + tp + q) * I + c];
@@ -205,7 +209,7 @@ template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void k_combine(
     const int32_t *__restrict__ idx, const float *__restrict__ gate, const int32_t *__restrict__ pos,
     const uint64_t *__restrict__ ptrs, const float *__restrict__ Y, int k, int d,
-    const float *residual, const float *__restrict__ host_part, float *out, void *out_act)
+    int E, int R, const float *residual, const float *__restrict__ host_part, float *out, void *out_act)
 {
     const int t = blockIdx.y;
     const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
@@ -214,10 +218,11 @@ __global__ __launch_bounds__(256) void k_combine(
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < k; ++j) {
         const int f = t * k + j;
-        if (!ptrs[idx[f]])
+        const int e = idx[f], p = pos[f];
+        if ((unsigned)e >= (unsigned)E || (unsigned)p >= (unsigned)R || !ptrs[e])
             continue;
         const float g = gate[f];
-        const float4 y = *reinterpret_cast<const float4 *>(Y + (size_t)pos[f] * d + c);
+        const float4 y = *reinterpret_cast<const float4 *>(Y + (size_t)p * d + c);
         s.x = fmaf(g, y.x, s.x);
         s.y = fmaf(g, y.y, s.y);
         s.z = fmaf(g, y.z, s.z);
@@ -254,13 +259,14 @@ int launch_decode_gateup(const ecf_shape &s, const ExpertTables &ex, const Route
     const int maxa = std::min(s.n_experts, R);
     constexpr int IB = 8, KP = 2;
     dim3 grid(s.inter / IB, maxa);
-    const size_t sh = sizeof(float) * std::min(kDecodeNT, T) * s.hidden;
+    const int ntp = std::min(kDecodeNT, T);  // an expert has at most T rows
+    const size_t sh = sizeof(float) * ntp * s.hidden;
     ProfScope p("decode_gateup", st);
     const bool wbf = s.w_dtype == ECF_BF16, abf = s.a_dtype == ECF_BF16;
 #define ECF_GU(WB, AB)                                                                              \
     hipLaunchKernelGGL((k_decode_gateup<WB, AB, IB, KP>), grid, dim3(256), sh, st, ex.ptrs,          \
                        ex.lay.off[0], ex.lay.off[1], o.active, o.n_active, o.offsets, o.perm, x,      \
-                       s.hidden, s.inter, s.top_k, H)
+                       s.hidden, s.inter, s.top_k, s.n_experts, R, ntp, H)
     if (wbf && abf)
         ECF_GU(true, true);
     else if (wbf)
@@ -281,14 +287,16 @@ int launch_decode_down(const ecf_shape &s, const ExpertTables &ex, const RouteOu
     const int maxa = std::min(s.n_experts, R);
     constexpr int OB = 32, KP = 1;
     dim3 grid(s.hidden / OB, maxa);
-    const size_t sh = sizeof(float) * std::min(kDecodeNT, T) * s.inter;
+    const int ntp = std::min(kDecodeNT, T);
+    const size_t sh = sizeof(float) * ntp * s.inter;
     ProfScope p("decode_down", st);
     if (s.w_dtype == ECF_BF16)
         hipLaunchKernelGGL((k_decode_down<true, OB, KP>), grid, dim3(256), sh, st, ex.ptrs, ex.lay.off[2],
-                           o.active, o.n_active, o.offsets, H, s.hidden, s.inter, Y);
+                           o.active, o.n_active, o.offsets, H, s.hidden, s.inter, s.n_experts, R, ntp, Y);
     else
         hipLaunchKernelGGL((k_decode_down<false, OB, KP>), grid, dim3(256), sh, st, ex.ptrs,
-                           ex.lay.off[2], o.active, o.n_active, o.offsets, H, s.hidden, s.inter, Y);
+                           ex.lay.off[2], o.active, o.n_active, o.offsets, H, s.hidden, s.inter, s.n_experts,
+                           R, ntp, Y);
     ECF_HIP_CHECK(hipGetLastError());
     return ECF_OK;
 }
@@ -301,10 +309,10 @@ int launch_combine(const ecf_shape &s, const ExpertTables &ex, const RouteOut &o
     ProfScope p("combine", st);
     if (s.a_dtype == ECF_BF16)
         hipLaunchKernelGGL((k_combine<true>), grid, dim3(256), 0, st, o.idx, o.gate, o.pos, ex.ptrs, Y,
-                           s.top_k, s.hidden, residual, host_part, out, out_act);
+                           s.top_k, s.hidden, s.n_experts, T * s.top_k, residual, host_part, out, out_act);
     else
         hipLaunchKernelGGL((k_combine<false>), grid, dim3(256), 0, st, o.idx, o.gate, o.pos, ex.ptrs, Y,
-                           s.top_k, s.hidden, residual, host_part, out, out_act);
+                           s.top_k, s.hidden, s.n_experts, T * s.top_k, residual, host_part, out, out_act);
     ECF_HIP_CHECK(hipGetLastError());
     return ECF_OK;
 }

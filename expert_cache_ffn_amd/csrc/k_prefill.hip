@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256) void k_gemm1_swiglu(
     const uint64_t *__restrict__ ptrs, size_t off_g, size_t off_u, size_t off_sg, size_t off_su,
     const int32_t *__restrict__ tiles, const int32_t *__restrict__ n_tiles,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm,
-    const uint16_t *__restrict__ x, int d, int I, int k, uint16_t *__restrict__ H)
+    const uint16_t *__restrict__ x, int d, int I, int k, int E, int R, uint16_t *__restrict__ H)
 {
     constexpr int BN = 64;
     __shared__ uint4 As[2][BM * 8];
@@ -132,11 +132,13 @@ __global__ __launch_bounds__(256) void k_gemm1_swiglu(
     if ((int)blockIdx.y >= *n_tiles)
         return;
     const int e = tiles[2 * blockIdx.y], m0 = tiles[2 * blockIdx.y + 1];
-    const uint64_t blob = ptrs[e];
-    if (!blob)
+    if ((unsigned)e >= (unsigned)E)  // routing metadata is produced on the device; never index past it
         return;
+    const uint64_t blob = ptrs[e];
     const int rb = offsets[e] + m0;
     const int mrows = min(BM, offsets[e + 1] - rb);
+    if (!blob || m0 < 0 || rb < 0 || mrows <= 0 || rb + mrows > R)
+        return;
     const int i0 = blockIdx.x * BN;
     const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
 
@@ -228,7 +230,7 @@ template <bool MX>
 __global__ __launch_bounds__(256) void k_gemm2_down(
     const uint64_t *__restrict__ ptrs, size_t off_d, size_t off_sd, const int32_t *__restrict__ tiles,
     const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ offsets,
-    const uint16_t *__restrict__ H, int d, int I, float *__restrict__ Y)
+    const uint16_t *__restrict__ H, int d, int I, int E, int R, float *__restrict__ Y)
 {
     constexpr int BN = 128;
     __shared__ uint4 As[2][BM * 8];
@@ -237,11 +239,13 @@ __global__ __launch_bounds__(256) void k_gemm2_down(
     if ((int)blockIdx.y >= *n_tiles)
         return;
     const int e = tiles[2 * blockIdx.y], m0 = tiles[2 * blockIdx.y + 1];
-    const uint64_t blob = ptrs[e];
-    if (!blob)
+    if ((unsigned)e >= (unsigned)E)  // routing metadata is produced on the device; never index past it
         return;
+    const uint64_t blob = ptrs[e];
     const int rb = offsets[e] + m0;
     const int mrows = min(BM, offsets[e + 1] - rb);
+    if (!blob || m0 < 0 || rb < 0 || mrows <= 0 || rb + mrows > R)
+        return;
     const int o0 = blockIdx.x * BN;
     const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
 
@@ -335,11 +339,11 @@ int launch_prefill_gemm1(const ecf_shape &s, const ExpertTables &ex, const Route
     if (s.w_dtype == ECF_MXFP4)
         hipLaunchKernelGGL((k_gemm1_swiglu<true>), grid, dim3(256), 0, st, ex.ptrs, ex.lay.off[0],
                            ex.lay.off[1], ex.lay.off[3], ex.lay.off[4], o.tiles, o.n_tiles, o.offsets,
-                           o.perm, (const uint16_t *)x, s.hidden, s.inter, s.top_k, H);
+                           o.perm, (const uint16_t *)x, s.hidden, s.inter, s.top_k, s.n_experts, T * s.top_k, H);
     else
         hipLaunchKernelGGL((k_gemm1_swiglu<false>), grid, dim3(256), 0, st, ex.ptrs, ex.lay.off[0],
                            ex.lay.off[1], ex.lay.off[3], ex.lay.off[4], o.tiles, o.n_tiles, o.offsets,
-                           o.perm, (const uint16_t *)x, s.hidden, s.inter, s.top_k, H);
+                           o.perm, (const uint16_t *)x, s.hidden, s.inter, s.top_k, s.n_experts, T * s.top_k, H);
     ECF_HIP_CHECK(hipGetLastError());
     return ECF_OK;
 }
@@ -351,10 +355,10 @@ int launch_prefill_gemm2(const ecf_shape &s, const ExpertTables &ex, const Route
     ProfScope p("prefill_gemm2", st);
     if (s.w_dtype == ECF_MXFP4)
         hipLaunchKernelGGL((k_gemm2_down<true>), grid, dim3(256), 0, st, ex.ptrs, ex.lay.off[2],
-                           ex.lay.off[5], o.tiles, o.n_tiles, o.offsets, H, s.hidden, s.inter, Y);
+                           ex.lay.off[5], o.tiles, o.n_tiles, o.offsets, H, s.hidden, s.inter, s.n_experts, T * s.top_k, Y);
     else
         hipLaunchKernelGGL((k_gemm2_down<false>), grid, dim3(256), 0, st, ex.ptrs, ex.lay.off[2],
-                           ex.lay.off[5], o.tiles, o.n_tiles, o.offsets, H, s.hidden, s.inter, Y);
+                           ex.lay.off[5], o.tiles, o.n_tiles, o.offsets, H, s.hidden, s.inter, s.n_experts, T * s.top_k, Y);
     ECF_HIP_CHECK(hipGetLastError());
     return ECF_OK;
 }

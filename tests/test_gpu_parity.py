@@ -171,3 +171,33 @@ def test_decode_and_prefill_paths_agree():
     rms = np.sqrt(np.mean(a["out"] ** 2))
     assert np.max(np.abs(a["out"] - b["out"])) <= TOL["bf16"] * rms
     assert np.array_equal(a["perm"], b["perm"])
+
+
+# ---- HIP graph capture of the all-resident decode forward ---------------------------------
+
+def test_graph_replay_matches_eager():
+    """The all-resident path is stream-ordered with no host sync, so it can be
+    captured; every replay (with eager work in between) must equal eager."""
+    from expert_cache_ffn_amd.layer import Layer
+    cfg = cfg_small(experts=16, top_k=4, cid=92)
+    c = Case(cfg, 8)
+    eager = c.run()["out"]
+    lay = Layer(c.shape, 8)
+    s = torch.cuda.Stream()
+    x = c.x.cuda().contiguous()
+    wr = c.router_w.cuda().contiguous()
+    out = torch.zeros((8, cfg.hidden), dtype=torch.float32, device="cuda")
+    with torch.cuda.stream(s):
+        a = lay.args(router_w=wr, expert_ptrs=c.pool.ptrs, stream=s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            rc = ecf.lib().moe_layer_forward(a, x.data_ptr(), 8, out.data_ptr(), None)
+        assert rc == 0
+    for rep in range(4):
+        out.fill_(float("nan"))
+        junk = torch.randn(1000, 1000, device="cuda") @ torch.randn(1000, 1000, device="cuda")
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), eager), f"replay {rep} differs"
+        del junk
