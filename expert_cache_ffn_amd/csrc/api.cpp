@@ -344,7 +344,7 @@ static int pick_path(const ecf_layer_args *a, int32_t T)
         return ECF_PATH_DECODE;
     if (a->shape.w_dtype == ECF_MXFP4)
         return ECF_PATH_PREFILL;
-    return T <= 64 ? ECF_PATH_DECODE : ECF_PATH_PREFILL;
+    return (T <= 64 || a->shape.inter % 128) ? ECF_PATH_DECODE : ECF_PATH_PREFILL;
 }
 
 // Expert-cache placement for one layer-step: read the routing back, look the
@@ -540,8 +540,8 @@ int moe_layer_forward(const ecf_layer_args *a, const void *d_x, int32_t T, float
             return set_error(ECF_ENOSPC, "workspace too small: %zu < %zu bytes for %d tokens", a->ws_bytes,
                              wl.total, T);
         const int path = pick_path(a, T);
-        if (path == ECF_PATH_PREFILL && (s.w_dtype == ECF_F32 || s.hidden % 128))
-            return set_error(ECF_EUNSUPPORTED, "the prefill path needs bf16/MXFP4 weights and d %% 128 == 0");
+        if (path == ECF_PATH_PREFILL && (s.w_dtype == ECF_F32 || s.inter % 128))
+            return set_error(ECF_EUNSUPPORTED, "the prefill path needs bf16/MXFP4 weights and inter %% 128 == 0");
         if (path == ECF_PATH_DECODE && s.w_dtype == ECF_MXFP4)
             return set_error(ECF_EUNSUPPORTED, "MXFP4 weights run on the prefill path");
         hipStream_t stream = (hipStream_t)a->stream;

@@ -61,9 +61,9 @@ const char *ecf_last_error(void);
 typedef enum { ECF_F32 = 0, ECF_BF16 = 1, ECF_MXFP4 = 2 } ecf_dtype;
 
 typedef struct {
-    int32_t hidden;      /* d: model width; multiple of 64 (of 128 for MXFP4 or the
-                            prefill path) */
-    int32_t inter;       /* I: expert intermediate width; multiple of 64 */
+    int32_t hidden;      /* d: model width; multiple of 256 */
+    int32_t inter;       /* I: expert intermediate width; multiple of 64 (of 128 for
+                            the prefill path, which MXFP4 weights always take) */
     int32_t n_experts;   /* E: routed experts per layer, 1..1024 */
     int32_t top_k;       /* k: experts per token, 1..min(E, 32) */
     int32_t w_dtype;     /* expert weight encoding, ecf_dtype */

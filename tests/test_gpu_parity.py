@@ -104,7 +104,7 @@ def test_residual_added():
 
 # ---- prefill bf16 (grouped MFMA GEMM) ---------------------------------------------------
 
-@pytest.mark.parametrize("T,E,k,I", [(300, 8, 2, 256), (1000, 4, 2, 128), (97, 32, 6, 192)])
+@pytest.mark.parametrize("T,E,k,I", [(300, 8, 2, 256), (1000, 4, 2, 128), (97, 32, 6, 384), (700, 3, 1, 256)])
 def test_prefill_bf16_ragged_tiles(T, E, k, I):
     cfg = cfg_small(experts=E, top_k=k, inter=I, logits="uniform", cid=70 + E)
     say(f"case: prefill bf16 T={T} E={E} k={k} I={I}")
