@@ -397,6 +397,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--cached-steps", type=int, default=12)
+    ap.add_argument("--decode-tokens", default="1,4,16",
+                    help="decode batch sizes (the headline is 16; others are reported alongside)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -410,17 +412,19 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     ecf.lib()
     wl = set(args.workloads.split(","))
-    dec, sample = bench_decode(torch, ecf, syn, (1, 4, 16), args.steps, args.warmup, use_graph=not args.no_graph)
-    head = dec[16]
-    also = {f"decode_T{T}": dec[T] for T in (1, 4)}
+    Ts = tuple(int(t) for t in args.decode_tokens.split(","))
+    head, also, cpu, sample = None, {}, None, None
+    if "decode" in wl:
+        dec, sample = bench_decode(torch, ecf, syn, Ts, args.steps, args.warmup, use_graph=not args.no_graph)
+        head = dec.get(16)
+        also.update({f"decode_T{T}": dec[T] for T in Ts if T != 16})
     if "prefill" in wl:
         also["prefill_bf16_T4096"] = bench_prefill(torch, ecf, syn, "prefill", max(5, args.steps // 20),
                                                    max(2, args.warmup // 5))
     if "prefill_fp4" in wl:
         also["prefill_mxfp4_T8192"] = bench_prefill(torch, ecf, syn, "prefill_fp4", max(5, args.steps // 20),
                                                     max(2, args.warmup // 5))
-    cpu = None
-    if not args.no_cpu_baseline:
+    if sample is not None and not args.no_cpu_baseline:
         log("cpu baseline: oracle on sampled decode batches")
         cpu = cpu_baseline_decode(torch, syn, sample)
         log(f"cpu baseline: {cpu['value']:.2f} tok/s on {cpu['cores']} threads")
@@ -431,6 +435,9 @@ def main():
     if "cached" in wl:
         also["cached_decode_43L_T16"] = bench_cached(torch, ecf, syn, steps=args.cached_steps,
                                                      warmup=args.cached_steps)
+    if head is None:  # a partial run (profiling): no headline line
+        print(json.dumps({"partial": True, "also": also}), flush=True)
+        return
 
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "decode_gateup_T16_traffic.json")

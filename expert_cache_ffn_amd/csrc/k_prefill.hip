@@ -13,9 +13,9 @@
 //          registers on matching accumulator fragments.
 //   GEMM2: Y = H . W_down^T (fp32), combined per token by k_combine.
 //
-// Block = 4 waves (2 x 2), tile 128 rows x 256 weight rows, BK = 64; each wave
-// owns 64 rows x 128 weight rows (2 x 4 MFMA 32x32 fragments, accumulators in
-// AGPRs).  Software pipeline of depth 2 through registers: the global loads
+// Block = 4 waves (2 x 2), tile 128 rows x BNT weight rows (BNT = 128 by
+// default), BK = 64; each wave owns 64 rows x BNT/2 weight rows (2 x BNT/64
+// MFMA 32x32 fragments).  Software pipeline of depth 2 through registers: the global loads
 // of k-tile kt+2 are issued before the MFMAs of k-tile kt, and stored to the
 // free LDS buffer after them, so two k-tiles of MFMA work cover each load's
 // latency.  (Direct global->LDS loads were measured against: the compiler
@@ -39,14 +39,13 @@ namespace ecf {
 
 namespace {
 constexpr int BM = kPrefillMT;  // 128 rows per tile
-constexpr int BN = 256;         // weight rows per block
 constexpr int BK = 64;          // reduction elements per stage
 
 __device__ __forceinline__ int swz(int row, int ch) { return row * 8 + (ch ^ (row & 7)); }
 
 // MXFP4 LDS tile: row = 32 bytes (two 16-B halves), halves swapped on odd
-// groups of 8 rows to spread the banks.
-__device__ __forceinline__ int mx_slot(int row, int half) { return row * 2 + (half ^ ((row >> 3) & 1)); }
+// groups of 4 rows, so 8 consecutive rows read at one half cover all banks.
+__device__ __forceinline__ int mx_slot(int row, int half) { return row * 2 + (half ^ ((row >> 2) & 1)); }
 
 __device__ __forceinline__ float e8m0_f(uint32_t s)
 {
@@ -57,20 +56,20 @@ __device__ __forceinline__ float e8m0_f(uint32_t s)
 // from a device table, so they would otherwise be generic/flat pointers).
 typedef const __attribute__((address_space(1))) u32x4_t *gptr16;
 typedef const __attribute__((address_space(1))) uint16_t *gptr2;
+typedef const __attribute__((address_space(1))) uint32_t *gptr4;
 __device__ __forceinline__ u32x4_t ldg16(const void *p) { return *(gptr16)(uintptr_t)p; }
 __device__ __forceinline__ uint32_t ldg2(const void *p) { return *(gptr2)(uintptr_t)p; }
+__device__ __forceinline__ uint32_t ldg4(const void *p) { return *(gptr4)(uintptr_t)p; }
 
 __device__ __forceinline__ bf16x8_t frag_bf16(const u32x4_t *tile, int row, int kc)
 {
     return __builtin_bit_cast(bf16x8_t, tile[swz(row, kc)]);
 }
 
-// 8 MXFP4 elements of row `row`, k-chunk kc (0..7) -> bf16x8 scaled by the block scale.
-__device__ __forceinline__ bf16x8_t frag_mx(const u32x4_t *tile, const uint8_t *sc, int row, int kc)
+// 8 MXFP4 elements (one dword of nibbles, element 2i in the low nibble of byte
+// i) -> bf16x8, each multiplied by the block scale s (exact: s is a power of 2).
+__device__ __forceinline__ bf16x8_t cvt_mx8(uint32_t w, float s)
 {
-    const uint32_t *t32 = reinterpret_cast<const uint32_t *>(tile);
-    const uint32_t w = t32[mx_slot(row, kc >> 2) * 4 + (kc & 3)];
-    const float s = e8m0_f(sc[row * 2 + (kc >> 2)]);
     const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0);
     const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1);
     const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2);
@@ -82,53 +81,67 @@ __device__ __forceinline__ bf16x8_t frag_mx(const u32x4_t *tile, const uint8_t *
 }
 
 // One stage of global data held in registers between load and LDS store.
-template <bool MX>
+// BNT = weight rows per block tile; NBL = 16-B B chunks per thread and stage.
+// A stage covers KS sub-tiles of BK = 64 reduction elements each.
+template <bool MX, int BNT, int KS>
 struct Stage {
-    u32x4_t a[4];             // A: rows (tid>>3) + 32q, chunk tid&7
-    u32x4_t b[MX ? 2 : 8];    // B bf16: rows (tid>>3) + 32q; MX: rows (tid>>1) + 128q, half tid&1
-    uint32_t s;               // MX: the two scale bytes of row tid
+    static constexpr int NBL = MX ? BNT / 128 : BNT / 32;
+    u32x4_t a[4 * KS];        // A: rows (tid>>3) + 32q, chunk tid&7, per sub-tile
+    u32x4_t b[NBL * KS];      // B bf16: rows (tid>>3) + 32q; MX: rows (tid>>1) + 128q, half tid&1
+    uint32_t s;               // MX: the 2*KS scale bytes of row tid (tid < BNT)
 };
 
-template <bool MX>
+template <bool MX, int BNT>
 struct Ptrs {
     const char *a[4];
-    const char *b[MX ? 2 : 8];
+    const char *b[MX ? BNT / 128 : BNT / 32];
     const uint8_t *s;
 };
 
-template <bool MX>
-__device__ __forceinline__ void gload(Stage<MX> &st, const Ptrs<MX> &p, int kt)
+template <bool MX, int BNT, int KS>
+__device__ __forceinline__ void gload(Stage<MX, BNT, KS> &st, const Ptrs<MX, BNT> &p, int kt, int tid)
 {
+    constexpr int NBL = Stage<MX, BNT, KS>::NBL;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-        st.a[q] = ldg16(p.a[q] + (size_t)kt * BK * 2);
-    if (MX) {
+    for (int sub = 0; sub < KS; ++sub) {
+        const size_t col = (size_t)(kt * KS + sub) * BK;  // first reduction element of the sub-tile
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
-            st.b[q] = ldg16(p.b[q] + (size_t)kt * BK / 2);
-        st.s = ldg2(p.s + (size_t)kt * 2);
-    } else {
+        for (int q = 0; q < 4; ++q)
+            st.a[sub * 4 + q] = ldg16(p.a[q] + col * 2);
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-            st.b[q] = ldg16(p.b[q] + (size_t)kt * BK * 2);
+        for (int q = 0; q < NBL; ++q)
+            st.b[sub * NBL + q] = ldg16(p.b[q] + (MX ? col / 2 : col * 2));
     }
+    if (MX && (BNT >= 256 || tid < BNT))
+        st.s = KS == 2 ? ldg4(p.s + (size_t)kt * 4) : ldg2(p.s + (size_t)kt * 2);
 }
 
-template <bool MX>
-__device__ __forceinline__ void sstore(const Stage<MX> &st, u32x4_t *As, u32x4_t *Bs, uint8_t *Sc, int tid)
+// Registers -> LDS.  MX scales are widened to fp32 here, once per row and stage.
+// Registers -> LDS.  Sub-tile `sub` of A sits at As + sub * BM * 8 and of B at
+// Bs + sub * (B tile size).  MX scales are widened to fp32 here, once per row
+// and stage, and stored group-major: Scf[group * BNT + row].
+template <bool MX, int BNT, int KS>
+__device__ __forceinline__ void sstore(const Stage<MX, BNT, KS> &st, u32x4_t *As, u32x4_t *Bs, float *Scf, int tid)
 {
+    constexpr int NBL = Stage<MX, BNT, KS>::NBL;
+    constexpr int BT = MX ? BNT * 2 : BNT * 8;  // 16-B slots of one B sub-tile
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-        As[swz((tid >> 3) + 32 * q, tid & 7)] = st.a[q];
-    if (MX) {
+    for (int sub = 0; sub < KS; ++sub) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
-            Bs[mx_slot((tid >> 1) + 128 * q, tid & 1)] = st.b[q];
-        *reinterpret_cast<uint16_t *>(Sc + tid * 2) = (uint16_t)st.s;
-    } else {
+        for (int q = 0; q < 4; ++q)
+            As[sub * BM * 8 + swz((tid >> 3) + 32 * q, tid & 7)] = st.a[sub * 4 + q];
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-            Bs[swz((tid >> 3) + 32 * q, tid & 7)] = st.b[q];
+        for (int q = 0; q < NBL; ++q) {
+            if (MX)
+                Bs[sub * BT + mx_slot((tid >> 1) + 128 * q, tid & 1)] = st.b[sub * NBL + q];
+            else
+                Bs[sub * BT + swz((tid >> 3) + 32 * q, tid & 7)] = st.b[sub * NBL + q];
+        }
+    }
+    if (MX && (BNT >= 256 || tid < BNT)) {
+#pragma unroll
+        for (int gi = 0; gi < 2 * KS; ++gi)
+            Scf[gi * BNT + tid] = e8m0_f((st.s >> (8 * gi)) & 0xffu);
     }
 }
 
@@ -141,21 +154,36 @@ __device__ __forceinline__ int xcd_item(int b, int total)
     const int x = b & 7, i = b >> 3, q = total >> 3, r = total & 7;
     return x * q + min(x, r) + i;
 }
+
+template <int V>
+struct IC {
+    static constexpr int value = V;
+};
 }  // namespace
 
 // MODE 1: GEMM1 + SwiGLU (A = x rows through perm, K = d, out H bf16 [R][I]).
 // MODE 2: GEMM2          (A = H rows,           K = I, out Y fp32 [R][d]).
-// grid = max tiles * NT blocks (1-D), NT = N / 128 (MODE 1) or d / 256 (MODE 2).
-template <int MODE, bool MX>
-__global__ __launch_bounds__(256, 1) void k_grouped_gemm(
+// BNT weight rows per block (MODE 1: BNT/2 gate + BNT/2 up rows), MINB blocks
+// per CU asked of the register allocator.
+// grid = max tiles * NT blocks (1-D), NT = I / (BNT/2) (MODE 1) or d / BNT (MODE 2).
+//
+// Reduction order inside a 64-wide k-tile: at MFMA step ks (0..3), lanes 0-31
+// feed k-chunk ks and lanes 32-63 feed k-chunk 4 + ks (8 elements each), for A
+// and B alike, so every chunk is used once.  Lane half g then reads the 32
+// MXFP4 elements 32g..32g+31 -- 16 bytes, exactly one E8M0 scale group -- with
+// a single LDS read per k-tile.
+template <int MODE, bool MX, int BNT, int MINB, int KS, int WM>
+__global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
     const uint64_t *__restrict__ ptrs, size_t off_w0, size_t off_w1, size_t off_s0, size_t off_s1,
     const int32_t *__restrict__ tiles, const int32_t *__restrict__ n_tiles,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm, const uint16_t *__restrict__ A,
     int K, int N, int lda, int k, int E, int R, int NT, void *__restrict__ out)
 {
-    __shared__ u32x4_t As[2][BM * 8];
-    __shared__ u32x4_t Bs[2][MX ? BN * 2 : BN * 8];
-    __shared__ uint8_t Sc[2][MX ? BN * 2 : 4];
+    constexpr int NCB = BNT / 64;  // 32-column MFMA blocks per wave
+    constexpr int BT = MX ? BNT * 2 : BNT * 8;  // 16-B slots of one B sub-tile
+    __shared__ u32x4_t As[2][KS * BM * 8];
+    __shared__ u32x4_t Bs[2][KS * BT];
+    __shared__ float Scf[2][MX ? 2 * KS * BNT : 4];
 
     const int item = xcd_item(blockIdx.x, *n_tiles * NT);
     if (item < 0)
@@ -169,23 +197,26 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm(
     const int mrows = min(BM, offsets[e + 1] - rb);
     if (!blob || m0 < 0 || rb < 0 || mrows <= 0 || rb + mrows > R)
         return;
-    const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
-    // MODE 1: this block's intermediate columns [n0, n0 + 128); MODE 2: outputs [n0, n0 + 256)
-    const int n0 = nt * (MODE == 1 ? BN / 2 : BN);
+    // WM waves along M (2: 2 x 2 layout, 64 rows per wave; 1: 1 x 4, 128 rows per
+    // wave, which halves the per-MFMA B-fragment work at the cost of A reads)
+    constexpr int WN = 4 / WM, WROWS = BM / WM, NMSMAX = WROWS / 32;
+    const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, wm = w / WN, wn = w % WN, g = l >> 5;
+    // MODE 1: this block's intermediate columns [n0, n0 + BNT/2); MODE 2: outputs [n0, n0 + BNT)
+    const int n0 = nt * (MODE == 1 ? BNT / 2 : BNT);
 
-    Ptrs<MX> p;
+    Ptrs<MX, BNT> p;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int row = min((tid >> 3) + 32 * q, mrows - 1);
         const size_t arow = MODE == 1 ? (size_t)(perm[rb + row] / k) : (size_t)(rb + row);
         p.a[q] = (const char *)(A + arow * lda + (tid & 7) * 8);
     }
-    // weight row r of the block's B tile (0..255) -> matrix row in the blob
+    // weight row r of the block's B tile -> (section, scale section, matrix row)
     auto brow = [&](int r, size_t &sec_off, size_t &sc_off) {
         if (MODE == 1) {
-            sec_off = r < BN / 2 ? off_w0 : off_w1;
-            sc_off = r < BN / 2 ? off_s0 : off_s1;
-            return n0 + (r & (BN / 2 - 1));
+            sec_off = r < BNT / 2 ? off_w0 : off_w1;
+            sc_off = r < BNT / 2 ? off_s0 : off_s1;
+            return n0 + (r & (BNT / 2 - 1));
         }
         sec_off = off_w0;
         sc_off = off_s0;
@@ -193,124 +224,172 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm(
     };
     if (MX) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < (MX ? BNT / 128 : BNT / 32); ++q) {
             size_t so, sco;
             const int r = brow((tid >> 1) + 128 * q, so, sco);
             p.b[q] = (const char *)blob + so + (size_t)r * (K / 2) + (tid & 1) * 16;
         }
         size_t so, sco;
-        const int r = brow(tid, so, sco);
+        const int r = brow(tid < BNT ? tid : 0, so, sco);
         p.s = (const uint8_t *)blob + sco + (size_t)r * (K / 32);
     } else {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < (MX ? BNT / 128 : BNT / 32); ++q) {
             size_t so, sco;
             const int r = brow((tid >> 3) + 32 * q, so, sco);
             p.b[q] = (const char *)blob + so + (size_t)r * K * 2 + (tid & 7) * 16;
         }
         p.s = nullptr;
     }
-    // B-tile rows of this wave's 4 column blocks
-    int bbase[4];
+    // B-tile rows (lane's row within each of this wave's column blocks)
+    int brw[NCB];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-        bbase[cb] = MODE == 1 ? (cb >> 1) * (BN / 2) + wn * 64 + (cb & 1) * 32 : wn * 128 + cb * 32;
-    // MFMA row blocks of this wave that hold real rows
-    const int nms = max(0, min(2, (mrows - wm * 64 + 31) / 32));
+    for (int cb = 0; cb < NCB; ++cb)
+        brw[cb] = (l & 31) + (MODE == 1 ? (cb < NCB / 2 ? wn * (BNT / 2 / WN) + cb * 32
+                                                       : BNT / 2 + wn * (BNT / 2 / WN) + (cb - NCB / 2) * 32)
+                                        : wn * (BNT / WN) + cb * 32);
+    const int nk = K / (BK * KS);
 
-    f32x16_t acc[2][4];
+    // The pipelined main loop and epilogue, instantiated per number of MFMA
+    // row blocks (0, 1, 2) this wave owns, so the loop body has no branches.
+    auto run = [&](auto nms_c) __attribute__((always_inline)) {
+        constexpr int NMS = decltype(nms_c)::value;
+        f32x16_t acc[NMSMAX][NCB];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < NMSMAX; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+            for (int b = 0; b < NCB; ++b)
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-                acc[a][b][j] = 0.f;
-
-    const int nk = K / BK;
-    Stage<MX> s0, s1;
-    gload<MX>(s0, p, 0);
-    if (nk > 1)
-        gload<MX>(s1, p, 1);
-    sstore<MX>(s0, As[0], Bs[0], Sc[0], tid);
-    __syncthreads();
-    // NXT holds k-tile kt+1 (loaded one iteration ago); FRE is free and receives
-    // k-tile kt+2.  Two copies of the body alternate the roles so both stages
-    // stay in named registers.
+                for (int j = 0; j < 16; ++j)
+                    acc[a][b][j] = 0.f;
+        Stage<MX, BNT, KS> s0, s1;
+        gload<MX, BNT, KS>(s0, p, 0, tid);
+        if (nk > 1)
+            gload<MX, BNT, KS>(s1, p, 1, tid);
+        sstore<MX, BNT, KS>(s0, As[0], Bs[0], Scf[0], tid);
+        __syncthreads();
+        // NXT holds k-tile kt+1 (loaded one iteration ago); FRE is free and
+        // receives k-tile kt+2.  Two copies of the body alternate the roles so
+        // both stages stay in named registers.
 #define ECF_GEMM_BODY(KT, NXT, FRE)                                                                  \
     {                                                                                               \
         const int cur = (KT) & 1;                                                                   \
         if ((KT) + 2 < nk)                                                                          \
-            gload<MX>(FRE, p, (KT) + 2);                                                            \
-        if (nms > 0) {                                                                              \
-            _Pragma("unroll") for (int ks = 0; ks < BK / 16; ++ks)                                  \
+            gload<MX, BNT, KS>(FRE, p, (KT) + 2, tid);                                              \
+        if (NMS > 0) {                                                                              \
+            _Pragma("unroll") for (int sub = 0; sub < KS; ++sub)                                    \
             {                                                                                       \
-                const int kc = ks * 2 + (l >> 5);                                                   \
-                bf16x8_t af[2], bfr[4];                                                             \
-                _Pragma("unroll") for (int ms = 0; ms < 2; ++ms) if (ms < nms) af[ms] =            \
-                    frag_bf16(As[cur], wm * 64 + ms * 32 + (l & 31), kc);                           \
-                _Pragma("unroll") for (int cb = 0; cb < 4; ++cb)                                    \
-                {                                                                                   \
-                    const int n = bbase[cb] + (l & 31);                                             \
-                    bfr[cb] = MX ? frag_mx(Bs[cur], Sc[cur], n, kc) : frag_bf16(Bs[cur], n, kc);     \
+                const u32x4_t *Asb = As[cur] + sub * BM * 8, *Bsb = Bs[cur] + sub * BT;             \
+                float bsc[NCB];                                                                     \
+                if (MX) {                                                                           \
+                    _Pragma("unroll") for (int cb = 0; cb < NCB; ++cb)                              \
+                        bsc[cb] = Scf[cur][(sub * 2 + g) * BNT + brw[cb]];                          \
                 }                                                                                   \
-                _Pragma("unroll") for (int ms = 0; ms < 2; ++ms) if (ms < nms)                      \
-                    _Pragma("unroll") for (int cb = 0; cb < 4; ++cb) acc[ms][cb] =                  \
-                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ms], bfr[cb], acc[ms][cb], 0, 0, 0); \
+                _Pragma("unroll") for (int ks = 0; ks < BK / 16; ++ks)                              \
+                {                                                                                   \
+                    const int kc = 4 * g + ks;                                                      \
+                    bf16x8_t af[NMSMAX], bfr[NCB];                                                  \
+                    _Pragma("unroll") for (int ms = 0; ms < NMS; ++ms) af[ms] =                    \
+                        frag_bf16(Asb, wm * WROWS + ms * 32 + (l & 31), kc);                        \
+                    _Pragma("unroll") for (int cb = 0; cb < NCB; ++cb) bfr[cb] =                    \
+                        MX ? cvt_mx8(reinterpret_cast<const uint32_t *>(Bsb)[mx_slot(brw[cb], g) * 4 + ks], \
+                                     bsc[cb])                                                       \
+                           : frag_bf16(Bsb, brw[cb], kc);                                           \
+                    _Pragma("unroll") for (int ms = 0; ms < NMS; ++ms)                              \
+                        _Pragma("unroll") for (int cb = 0; cb < NCB; ++cb) acc[ms][cb] =            \
+                            __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ms], bfr[cb], acc[ms][cb], 0, 0, 0); \
+                }                                                                                   \
             }                                                                                       \
         }                                                                                           \
         if ((KT) + 1 < nk)                                                                          \
-            sstore<MX>(NXT, As[cur ^ 1], Bs[cur ^ 1], Sc[cur ^ 1], tid);                            \
+            sstore<MX, BNT, KS>(NXT, As[cur ^ 1], Bs[cur ^ 1], Scf[cur ^ 1], tid);                  \
         __syncthreads();                                                                            \
     }
-    for (int kt = 0; kt < nk; kt += 2) {
-        ECF_GEMM_BODY(kt, s1, s0)
-        if (kt + 1 < nk)
-            ECF_GEMM_BODY(kt + 1, s0, s1)
-    }
+        for (int kt = 0; kt < nk; kt += 2) {
+            ECF_GEMM_BODY(kt, s1, s0)
+            if (kt + 1 < nk)
+                ECF_GEMM_BODY(kt + 1, s0, s1)
+        }
 #undef ECF_GEMM_BODY
-
-    // epilogue: a lane holds rows (j/4)*8 + (l/32)*4 + j%4 of column l%32 of each fragment
+        // epilogue: a lane holds rows (j/4)*8 + (l/32)*4 + j%4 of column l%32 of each fragment
 #pragma unroll
-    for (int ms = 0; ms < 2; ++ms) {
-        if (ms >= nms)
-            continue;
+        for (int ms = 0; ms < NMS; ++ms) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int m = wm * 64 + ms * 32 + (j >> 2) * 8 + (l >> 5) * 4 + (j & 3);
-            if (m >= mrows)
-                continue;
-            if (MODE == 1) {
-                uint16_t *H = (uint16_t *)out + (size_t)(rb + m) * N + n0 + wn * 64 + (l & 31);
-                H[0] = f_to_bf(silu_mul(acc[ms][0][j], acc[ms][2][j]));
-                H[32] = f_to_bf(silu_mul(acc[ms][1][j], acc[ms][3][j]));
-            } else {
-                float *Y = (float *)out + (size_t)(rb + m) * N + n0 + wn * 128 + (l & 31);
+            for (int j = 0; j < 16; ++j) {
+                const int m = wm * WROWS + ms * 32 + (j >> 2) * 8 + (l >> 5) * 4 + (j & 3);
+                if (m >= mrows)
+                    continue;
+                if (MODE == 1) {
+                    uint16_t *H = (uint16_t *)out + (size_t)(rb + m) * N + n0 + wn * (BNT / 2 / WN) + (l & 31);
 #pragma unroll
-                for (int cb = 0; cb < 4; ++cb)
-                    Y[cb * 32] = acc[ms][cb][j];
+                    for (int cb = 0; cb < NCB / 2; ++cb)
+                        H[cb * 32] = f_to_bf(silu_mul(acc[ms][cb][j], acc[ms][cb + NCB / 2][j]));
+                } else {
+                    float *Y = (float *)out + (size_t)(rb + m) * N + n0 + wn * (BNT / WN) + (l & 31);
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb)
+                        Y[cb * 32] = acc[ms][cb][j];
+                }
             }
         }
+    };
+    // MFMA row blocks of this wave that hold real rows (uniform over the wave)
+    // (with WM = 1 a block of 65..96 rows runs 4 row blocks: one wasted, one fewer instance)
+    const int nms = __builtin_amdgcn_readfirstlane(max(0, min(NMSMAX, (mrows - wm * WROWS + 31) / 32)));
+    if (WM == 1) {
+        if (nms > 2)
+            run(IC<NMSMAX>{});
+        else if (nms == 2)
+            run(IC<2>{});
+        else
+            run(IC<1>{});
+    } else {
+        if (nms == 2)
+            run(IC<2>{});
+        else if (nms == 1)
+            run(IC<1>{});
+        else
+            run(IC<0>{});
     }
 }
 
 // ---------------------------------------------------------------------------------
 
+// Tile choice per weight format, measured on MI355X (C4 bf16 and C5 MXFP4
+// prefill layers): 128-weight-row N-tiles, two blocks per CU, one 64-wide
+// sub-tile per stage, 2 x 2 waves.  Wider tiles, two-sub-tile stages and a
+// 1 x 4 wave layout were each slower or spilled registers.
+#ifndef ECF_BF16_BNT
+#define ECF_BF16_BNT 128
+#define ECF_BF16_MINB 2
+#define ECF_BF16_KS 1
+#define ECF_BF16_WM 2
+#endif
+#ifndef ECF_MX_BNT
+#define ECF_MX_BNT 128
+#define ECF_MX_MINB 2
+#define ECF_MX_KS 1
+#define ECF_MX_WM 2
+#endif
+
 int launch_prefill_gemm1(const ecf_shape &s, const ExpertTables &ex, const RouteOut &o, const void *x,
                          int T, uint16_t *H, hipStream_t st)
 {
-    const int NT = s.inter / (BN / 2);
+    const bool mx = s.w_dtype == ECF_MXFP4;
+    const int bnt = mx ? ECF_MX_BNT : ECF_BF16_BNT;
+    const int NT = s.inter / (bnt / 2);
     const int nblk = max_tiles(s, T) * NT;
     ProfScope p("prefill_gemm1", st);
-#define ECF_G1(MXV)                                                                                  \
-    hipLaunchKernelGGL((k_grouped_gemm<1, MXV>), dim3(nblk), dim3(256), 0, st, ex.ptrs, ex.lay.off[0], \
-                       ex.lay.off[1], ex.lay.off[3], ex.lay.off[4], o.tiles, o.n_tiles, o.offsets, o.perm, \
-                       (const uint16_t *)x, s.hidden, s.inter, s.hidden, s.top_k, s.n_experts, T * s.top_k,  \
-                       NT, (void *)H)
-    if (s.w_dtype == ECF_MXFP4)
-        ECF_G1(true);
+#define ECF_G1(MXV, BNV, MBV, KSV, WMV)                                                                    \
+    hipLaunchKernelGGL((k_grouped_gemm<1, MXV, BNV, MBV, KSV, WMV>), dim3(nblk), dim3(256), 0, st, ex.ptrs,  \
+                       ex.lay.off[0], ex.lay.off[1], ex.lay.off[3], ex.lay.off[4], o.tiles, o.n_tiles,         \
+                       o.offsets, o.perm, (const uint16_t *)x, s.hidden, s.inter, s.hidden, s.top_k,         \
+                       s.n_experts, T * s.top_k, NT, (void *)H)
+    // K = d; a stage of KS sub-tiles needs d % (64 * KS) == 0 (d is a multiple of 256)
+    if (mx)
+        ECF_G1(true, ECF_MX_BNT, ECF_MX_MINB, ECF_MX_KS, ECF_MX_WM);
     else
-        ECF_G1(false);
+        ECF_G1(false, ECF_BF16_BNT, ECF_BF16_MINB, ECF_BF16_KS, ECF_BF16_WM);
 #undef ECF_G1
     ECF_HIP_CHECK(hipGetLastError());
     return ECF_OK;
@@ -319,17 +398,28 @@ int launch_prefill_gemm1(const ecf_shape &s, const ExpertTables &ex, const Route
 int launch_prefill_gemm2(const ecf_shape &s, const ExpertTables &ex, const RouteOut &o, const uint16_t *H,
                          int T, float *Y, hipStream_t st)
 {
-    const int NT = s.hidden / BN;
+    const bool mx = s.w_dtype == ECF_MXFP4;
+    const int bnt = mx ? ECF_MX_BNT : ECF_BF16_BNT;
+    const int NT = s.hidden / bnt;
     const int nblk = max_tiles(s, T) * NT;
     ProfScope p("prefill_gemm2", st);
-#define ECF_G2(MXV)                                                                                  \
-    hipLaunchKernelGGL((k_grouped_gemm<2, MXV>), dim3(nblk), dim3(256), 0, st, ex.ptrs, ex.lay.off[2], \
-                       ex.lay.off[2], ex.lay.off[5], ex.lay.off[5], o.tiles, o.n_tiles, o.offsets, o.perm, H, \
-                       s.inter, s.hidden, s.inter, s.top_k, s.n_experts, T * s.top_k, NT, (void *)Y)
-    if (s.w_dtype == ECF_MXFP4)
-        ECF_G2(true);
-    else
-        ECF_G2(false);
+#define ECF_G2(MXV, BNV, MBV, KSV, WMV)                                                                    \
+    hipLaunchKernelGGL((k_grouped_gemm<2, MXV, BNV, MBV, KSV, WMV>), dim3(nblk), dim3(256), 0, st, ex.ptrs,  \
+                       ex.lay.off[2], ex.lay.off[2], ex.lay.off[5], ex.lay.off[5], o.tiles, o.n_tiles,         \
+                       o.offsets, o.perm, H, s.inter, s.hidden, s.inter, s.top_k, s.n_experts, T * s.top_k,  \
+                       NT, (void *)Y)
+    // K = I; two-sub-tile stages only when I % 128 == 0
+    if (mx) {
+        if (s.inter % (64 * ECF_MX_KS) == 0)
+            ECF_G2(true, ECF_MX_BNT, ECF_MX_MINB, ECF_MX_KS, ECF_MX_WM);
+        else
+            ECF_G2(true, ECF_MX_BNT, ECF_MX_MINB, 1, ECF_MX_WM);
+    } else {
+        if (s.inter % (64 * ECF_BF16_KS) == 0)
+            ECF_G2(false, ECF_BF16_BNT, ECF_BF16_MINB, ECF_BF16_KS, ECF_BF16_WM);
+        else
+            ECF_G2(false, ECF_BF16_BNT, ECF_BF16_MINB, 1, ECF_BF16_WM);
+    }
 #undef ECF_G2
     ECF_HIP_CHECK(hipGetLastError());
     return ECF_OK;
