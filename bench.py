@@ -397,6 +397,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--cached-steps", type=int, default=12)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="first run one plain 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--decode-tokens", default="1,4,16",
                     help="decode batch sizes (the headline is 16; others are reported alongside)")
     args = ap.parse_args()
@@ -411,6 +413,14 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     ecf.lib()
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 1 GiB device to device")
+        del src, dst
     wl = set(args.workloads.split(","))
     Ts = tuple(int(t) for t in args.decode_tokens.split(","))
     head, also, cpu, sample = None, {}, None, None
