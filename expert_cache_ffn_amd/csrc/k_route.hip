@@ -199,6 +199,37 @@ __device__ int block_excl_scan(int v, int *sh, int *total)
     return res;
 }
 
+// block_excl_scan for 64-bit values (sums of packed bit fields).
+__device__ unsigned long long block_excl_scan64(unsigned long long v, unsigned long long *sh,
+                                                unsigned long long *total)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    unsigned long long x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const unsigned long long y = __shfl_up(x, off, 64);
+        if (lane >= off)
+            x += y;
+    }
+    if (lane == 63)
+        sh[w] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned long long run = 0;
+        for (int i = 0; i < nw; ++i) {
+            const unsigned long long t = sh[i];
+            sh[i] = run;
+            run += t;
+        }
+        sh[16] = run;
+    }
+    __syncthreads();
+    const unsigned long long res = sh[w] + x - v;
+    *total = sh[16];
+    __syncthreads();
+    return res;
+}
+
 // Lanes of the wave whose key equals this lane's key (valid lanes only).
 __device__ __forceinline__ uint64_t match_peers(int key, bool valid, int nbits)
 {
@@ -259,7 +290,7 @@ __global__ __launch_bounds__(1024) void k_route_small(
     const int R = T * k;
     int *sidx = smem;
     int *hist = smem + R;
-    int *sc = hist + E;
+    __shared__ unsigned long long sc[17];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     for (int t = wv; t < T; t += 16)
         topk_wave<MAXS>(logits + (size_t)t * E, E, k, renorm, lane, idx + (size_t)t * k,
@@ -270,12 +301,15 @@ __global__ __launch_bounds__(1024) void k_route_small(
     for (int f = tid; f < R; f += 1024)
         atomicAdd(&hist[sidx[f]], 1);
     __syncthreads();
+    // one scan of three packed fields: rows (bits 0..20), active experts
+    // (21..41) and prefill tiles (42..62); each is at most R + E < 2^21
     const int c = tid < E ? hist[tid] : 0;
-    int tot, na, ntt;
-    const int off = block_excl_scan(c, sc, &tot);
-    const int aoff = block_excl_scan(c > 0 ? 1 : 0, sc, &na);
     const int nte = (c + MT - 1) / MT;
-    const int toff = block_excl_scan(nte, sc, &ntt);
+    constexpr unsigned long long M21 = (1ull << 21) - 1;
+    unsigned long long tot;
+    const unsigned long long run = block_excl_scan64(
+        (unsigned long long)c | ((unsigned long long)(c > 0) << 21) | ((unsigned long long)nte << 42), sc, &tot);
+    const int off = (int)(run & M21), aoff = (int)((run >> 21) & M21), toff = (int)(run >> 42);
     if (tid < E) {
         counts[tid] = c;
         offsets[tid] = off;
@@ -285,15 +319,13 @@ __global__ __launch_bounds__(1024) void k_route_small(
             tiles[2 * (toff + m)] = tid;
             tiles[2 * (toff + m) + 1] = m * MT;
         }
+        hist[tid] = off;  // scatter base; only this thread read hist[tid] since the last barrier
     }
     if (tid == 0) {
-        offsets[E] = tot;
-        *n_active = na;
-        *n_tiles = ntt;
+        offsets[E] = (int)(tot & M21);
+        *n_active = (int)((tot >> 21) & M21);
+        *n_tiles = (int)(tot >> 42);
     }
-    __syncthreads();
-    if (tid < E)
-        hist[tid] = off;
     __syncthreads();
     if (wv == 0)
         stable_scatter_wave(sidx, nullptr, 0, R, hist, key_bits(E), lane, perm, pos);
@@ -413,7 +445,7 @@ int launch_route(const ecf_shape &s, const float *logits, int T, const RouteOut 
     const int maxs = (E + 63) / 64;
     if (R <= kSmallRouteRows) {
         ProfScope p("route_small", st);
-        const size_t sh = sizeof(int) * (size_t)(R + E + 17);
+        const size_t sh = sizeof(int) * (size_t)(R + E);
 #define ECF_ROUTE_SMALL(MS)                                                                       \
     hipLaunchKernelGGL((k_route_small<MS>), dim3(1), dim3(1024), sh, st, logits, T, E, k,         \
                        s.renorm_topk, kPrefillMT, o.idx, o.gate, o.counts, o.offsets, o.perm,      \
