@@ -13,18 +13,17 @@
 //          registers on matching accumulator fragments.
 //   GEMM2: Y = H . W_down^T (fp32), combined per token by k_combine.
 //
-// Block = 4 waves (2 x 2), tile 128 rows x BNT weight rows (BNT = 128 by
-// default), BK = 64; each wave owns 64 rows x BNT/2 weight rows (2 x BNT/64
-// MFMA 32x32 fragments).  Software pipeline of depth 2 through registers: the global loads
-// of k-tile kt+2 are issued before the MFMAs of k-tile kt, and stored to the
-// free LDS buffer after them, so two k-tiles of MFMA work cover each load's
-// latency.  (Direct global->LDS loads were measured against: the compiler
+// Block = 4 waves (2 x 2), tile 128 rows x BNT weight rows (BNT = 128 for bf16,
+// 256 for MXFP4), BK = 64; each wave owns 64 rows x BNT/2 weight rows (2 x
+// BNT/64 MFMA 32x32 fragments).  Software pipeline of depth 2 through
+// registers: the global loads of k-tile kt+2 are issued before the MFMAs of
+// k-tile kt, and stored to the free LDS buffer after them, so over a k-tile of
+// MFMA work covers each load's latency.  (Direct global->LDS loads were measured against: the compiler
 // cannot tell which in-flight LDS DMA a later LDS read depends on and drains
 // them all, which serialises the pipeline.)
 //
-// bf16 rows of 64 elements (eight 16-B chunks) sit in LDS with chunk c of row r
-// at slot c ^ (r & 7), so the 32 rows one MFMA operand read touches spread over
-// the banks.  MXFP4 weights stay 4-bit in LDS (a quarter of the bf16 bytes) and
+// bf16 rows of 64 elements (eight 16-B chunks) sit in LDS XOR-swizzled (see
+// swz), so the 32 rows one MFMA operand read touches spread over the banks.  MXFP4 weights stay 4-bit in LDS (a quarter of the bf16 bytes) and
 // are expanded in registers by v_cvt_scalef32_pk_bf16_fp4, which applies the
 // E8M0 block scale exactly; products run on bf16 MFMA.
 //
@@ -41,11 +40,17 @@ namespace {
 constexpr int BM = kPrefillMT;  // 128 rows per tile
 constexpr int BK = 64;          // reduction elements per stage
 
-__device__ __forceinline__ int swz(int row, int ch) { return row * 8 + (ch ^ (row & 7)); }
+// bf16 tile rows of eight 16-B chunks; chunk c of row r sits at c ^ (r & 7) ^ bit 3
+// of r.  A 16-B-per-lane read of one chunk over rows r0..r0+15 then touches 16
+// distinct 16-B bank groups mod 256 B (and any 8 aligned rows 8 distinct groups
+// mod 128 B), so it is conflict-free whether the LDS serves 8 or 16 lanes of a
+// 128-bit access per cycle.
+__device__ __forceinline__ int swz(int row, int ch) { return row * 8 + (ch ^ (row & 7) ^ ((row >> 3) & 1)); }
 
-// MXFP4 LDS tile: row = 32 bytes (two 16-B halves), halves swapped on odd
-// groups of 4 rows, so 8 consecutive rows read at one half cover all banks.
-__device__ __forceinline__ int mx_slot(int row, int half) { return row * 2 + (half ^ ((row >> 2) & 1)); }
+// MXFP4 LDS tile: row = 32 bytes (two 16-B halves); the halves swap with bit 2
+// xor bit 3 of the row, so one half over 16 consecutive rows (or 8 aligned
+// rows) covers distinct bank groups.
+__device__ __forceinline__ int mx_slot(int row, int half) { return row * 2 + (half ^ (((row >> 2) ^ (row >> 3)) & 1)); }
 
 __device__ __forceinline__ float e8m0_f(uint32_t s)
 {
@@ -60,6 +65,8 @@ typedef const __attribute__((address_space(1))) uint32_t *gptr4;
 __device__ __forceinline__ u32x4_t ldg16(const void *p) { return *(gptr16)(uintptr_t)p; }
 __device__ __forceinline__ uint32_t ldg2(const void *p) { return *(gptr2)(uintptr_t)p; }
 __device__ __forceinline__ uint32_t ldg4(const void *p) { return *(gptr4)(uintptr_t)p; }
+typedef const __attribute__((address_space(1))) uint8_t *gptr1;
+__device__ __forceinline__ uint32_t ldg1(const void *p) { return *(gptr1)(uintptr_t)p; }
 
 __device__ __forceinline__ bf16x8_t frag_bf16(const u32x4_t *tile, int row, int kc)
 {
@@ -83,25 +90,30 @@ __device__ __forceinline__ bf16x8_t cvt_mx8(uint32_t w, float s)
 // One stage of global data held in registers between load and LDS store.
 // BNT = weight rows per block tile; NBL = 16-B B chunks per thread and stage.
 // A stage covers KS sub-tiles of BK = 64 reduction elements each.
-template <bool MX, int BNT, int KS>
+// MXFP4 weights either stay 4-bit in LDS and are expanded at every MFMA step
+// (DQ = false), or are expanded to bf16 once, when the stage is written to LDS
+// (DQ = true; the B tile is then laid out like a bf16 one).
+template <bool MX, bool DQ, int BNT, int KS>
 struct Stage {
     static constexpr int NBL = MX ? BNT / 128 : BNT / 32;
     u32x4_t a[4 * KS];        // A: rows (tid>>3) + 32q, chunk tid&7, per sub-tile
     u32x4_t b[NBL * KS];      // B bf16: rows (tid>>3) + 32q; MX: rows (tid>>1) + 128q, half tid&1
-    uint32_t s;               // MX: the 2*KS scale bytes of row tid (tid < BNT)
+    uint32_t s;               // MX, !DQ: the 2*KS scale bytes of row tid (tid < BNT)
+    uint32_t sb[MX && DQ ? NBL * KS : 1];  // MX, DQ: the scale byte of each B chunk
 };
 
-template <bool MX, int BNT>
+template <bool MX, bool DQ, int BNT>
 struct Ptrs {
     const char *a[4];
     const char *b[MX ? BNT / 128 : BNT / 32];
-    const uint8_t *s;
+    const uint8_t *s;                          // !DQ: scales of row tid
+    const uint8_t *sq[MX && DQ ? BNT / 128 : 1];  // DQ: scales of chunk q's row, at its half
 };
 
-template <bool MX, int BNT, int KS>
-__device__ __forceinline__ void gload(Stage<MX, BNT, KS> &st, const Ptrs<MX, BNT> &p, int kt, int tid)
+template <bool MX, bool DQ, int BNT, int KS>
+__device__ __forceinline__ void gload(Stage<MX, DQ, BNT, KS> &st, const Ptrs<MX, DQ, BNT> &p, int kt, int tid)
 {
-    constexpr int NBL = Stage<MX, BNT, KS>::NBL;
+    constexpr int NBL = Stage<MX, DQ, BNT, KS>::NBL;
 #pragma unroll
     for (int sub = 0; sub < KS; ++sub) {
         const size_t col = (size_t)(kt * KS + sub) * BK;  // first reduction element of the sub-tile
@@ -109,22 +121,30 @@ __device__ __forceinline__ void gload(Stage<MX, BNT, KS> &st, const Ptrs<MX, BNT
         for (int q = 0; q < 4; ++q)
             st.a[sub * 4 + q] = ldg16(p.a[q] + col * 2);
 #pragma unroll
-        for (int q = 0; q < NBL; ++q)
+        for (int q = 0; q < NBL; ++q) {
             st.b[sub * NBL + q] = ldg16(p.b[q] + (MX ? col / 2 : col * 2));
+            if (MX && DQ)
+                st.sb[sub * NBL + q] = ldg1(p.sq[q] + col / 32);
+        }
     }
-    if (MX && (BNT >= 256 || tid < BNT))
+    // every thread loads (threads past BNT re-read row 0's scales), so the number
+    // of loads in flight is the same on every path and the compiler's load
+    // counters can wait for exactly the older stage
+    if (MX && !DQ)
         st.s = KS == 2 ? ldg4(p.s + (size_t)kt * 4) : ldg2(p.s + (size_t)kt * 2);
 }
 
-// Registers -> LDS.  MX scales are widened to fp32 here, once per row and stage.
 // Registers -> LDS.  Sub-tile `sub` of A sits at As + sub * BM * 8 and of B at
-// Bs + sub * (B tile size).  MX scales are widened to fp32 here, once per row
-// and stage, and stored group-major: Scf[group * BNT + row].
-template <bool MX, int BNT, int KS>
-__device__ __forceinline__ void sstore(const Stage<MX, BNT, KS> &st, u32x4_t *As, u32x4_t *Bs, float *Scf, int tid)
+// Bs + sub * (B tile size).  MX, !DQ: scales are widened to fp32 here, once per
+// row and stage, and stored group-major: Scf[group * (BNT + 32) + row] (the pad
+// puts the two lane halves' reads on different banks).  MX, DQ: each thread
+// expands its 32 weights (one scale group) to four bf16 chunks.
+template <bool MX, bool DQ, int BNT, int KS>
+__device__ __forceinline__ void sstore(const Stage<MX, DQ, BNT, KS> &st, u32x4_t *As, u32x4_t *Bs, float *Scf,
+                                       int tid)
 {
-    constexpr int NBL = Stage<MX, BNT, KS>::NBL;
-    constexpr int BT = MX ? BNT * 2 : BNT * 8;  // 16-B slots of one B sub-tile
+    constexpr int NBL = Stage<MX, DQ, BNT, KS>::NBL;
+    constexpr int BT = MX && !DQ ? BNT * 2 : BNT * 8;  // 16-B slots of one B sub-tile
 #pragma unroll
     for (int sub = 0; sub < KS; ++sub) {
 #pragma unroll
@@ -132,16 +152,24 @@ __device__ __forceinline__ void sstore(const Stage<MX, BNT, KS> &st, u32x4_t *As
             As[sub * BM * 8 + swz((tid >> 3) + 32 * q, tid & 7)] = st.a[sub * 4 + q];
 #pragma unroll
         for (int q = 0; q < NBL; ++q) {
-            if (MX)
+            if (MX && DQ) {
+                const int row = (tid >> 1) + 128 * q, h = tid & 1;
+                const float sc = e8m0_f(st.sb[sub * NBL + q]);
+                const u32x4_t w = st.b[sub * NBL + q];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    Bs[sub * BT + swz(row, 4 * h + i)] = __builtin_bit_cast(u32x4_t, cvt_mx8(w[i], sc));
+            } else if (MX) {
                 Bs[sub * BT + mx_slot((tid >> 1) + 128 * q, tid & 1)] = st.b[sub * NBL + q];
-            else
+            } else {
                 Bs[sub * BT + swz((tid >> 3) + 32 * q, tid & 7)] = st.b[sub * NBL + q];
+            }
         }
     }
-    if (MX && (BNT >= 256 || tid < BNT)) {
+    if (MX && !DQ && (BNT >= 256 || tid < BNT)) {
 #pragma unroll
         for (int gi = 0; gi < 2 * KS; ++gi)
-            Scf[gi * BNT + tid] = e8m0_f((st.s >> (8 * gi)) & 0xffu);
+            Scf[gi * (BNT + 32) + tid] = e8m0_f((st.s >> (8 * gi)) & 0xffu);
     }
 }
 
@@ -172,7 +200,7 @@ struct IC {
 // and B alike, so every chunk is used once.  Lane half g then reads the 32
 // MXFP4 elements 32g..32g+31 -- 16 bytes, exactly one E8M0 scale group -- with
 // a single LDS read per k-tile.
-template <int MODE, bool MX, int BNT, int MINB, int KS, int WM>
+template <int MODE, bool MX, int BNT, int MINB, int KS, int WM, bool DQ>
 __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
     const uint64_t *__restrict__ ptrs, size_t off_w0, size_t off_w1, size_t off_s0, size_t off_s1,
     const int32_t *__restrict__ tiles, const int32_t *__restrict__ n_tiles,
@@ -180,10 +208,11 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
     int K, int N, int lda, int k, int E, int R, int NT, void *__restrict__ out)
 {
     constexpr int NCB = BNT / 64;  // 32-column MFMA blocks per wave
-    constexpr int BT = MX ? BNT * 2 : BNT * 8;  // 16-B slots of one B sub-tile
+    constexpr bool MXL = MX && !DQ;  // 4-bit weights in LDS, expanded per MFMA step
+    constexpr int BT = MXL ? BNT * 2 : BNT * 8;  // 16-B slots of one B sub-tile
     __shared__ u32x4_t As[2][KS * BM * 8];
     __shared__ u32x4_t Bs[2][KS * BT];
-    __shared__ float Scf[2][MX ? 2 * KS * BNT : 4];
+    __shared__ float Scf[2][MXL ? 2 * KS * (BNT + 32) : 4];
 
     const int item = xcd_item(blockIdx.x, *n_tiles * NT);
     if (item < 0)
@@ -204,7 +233,7 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
     // MODE 1: this block's intermediate columns [n0, n0 + BNT/2); MODE 2: outputs [n0, n0 + BNT)
     const int n0 = nt * (MODE == 1 ? BNT / 2 : BNT);
 
-    Ptrs<MX, BNT> p;
+    Ptrs<MX, DQ, BNT> p;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int row = min((tid >> 3) + 32 * q, mrows - 1);
@@ -228,6 +257,8 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
             size_t so, sco;
             const int r = brow((tid >> 1) + 128 * q, so, sco);
             p.b[q] = (const char *)blob + so + (size_t)r * (K / 2) + (tid & 1) * 16;
+            if (DQ)
+                p.sq[MX && DQ ? q : 0] = (const uint8_t *)blob + sco + (size_t)r * (K / 32) + (tid & 1);
         }
         size_t so, sco;
         const int r = brow(tid < BNT ? tid : 0, so, sco);
@@ -262,28 +293,30 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
 #pragma unroll
                 for (int j = 0; j < 16; ++j)
                     acc[a][b][j] = 0.f;
-        Stage<MX, BNT, KS> s0, s1;
-        gload<MX, BNT, KS>(s0, p, 0, tid);
-        if (nk > 1)
-            gload<MX, BNT, KS>(s1, p, 1, tid);
-        sstore<MX, BNT, KS>(s0, As[0], Bs[0], Scf[0], tid);
+        Stage<MX, DQ, BNT, KS> s0, s1;
+        gload<MX, DQ, BNT, KS>(s0, p, 0, tid);
+        gload<MX, DQ, BNT, KS>(s1, p, 1, tid);
+        sstore<MX, DQ, BNT, KS>(s0, As[0], Bs[0], Scf[0], tid);
         __syncthreads();
         // NXT holds k-tile kt+1 (loaded one iteration ago); FRE is free and
         // receives k-tile kt+2.  Two copies of the body alternate the roles so
-        // both stages stay in named registers.
+        // both stages stay in named registers.  Loads and stores are issued on
+        // every iteration (nk is even and >= 2; past the end the last k-tile is
+        // re-read into a buffer nobody reads): branch-free, the compiler's
+        // load counters wait only for the older stage, which keeps two k-tiles
+        // of loads in flight.
 #define ECF_GEMM_BODY(KT, NXT, FRE)                                                                  \
     {                                                                                               \
         const int cur = (KT) & 1;                                                                   \
-        if ((KT) + 2 < nk)                                                                          \
-            gload<MX, BNT, KS>(FRE, p, (KT) + 2, tid);                                              \
+        gload<MX, DQ, BNT, KS>(FRE, p, min((KT) + 2, nk - 1), tid);                                 \
         if (NMS > 0) {                                                                              \
             _Pragma("unroll") for (int sub = 0; sub < KS; ++sub)                                    \
             {                                                                                       \
                 const u32x4_t *Asb = As[cur] + sub * BM * 8, *Bsb = Bs[cur] + sub * BT;             \
                 float bsc[NCB];                                                                     \
-                if (MX) {                                                                           \
+                if (MXL) {                                                                          \
                     _Pragma("unroll") for (int cb = 0; cb < NCB; ++cb)                              \
-                        bsc[cb] = Scf[cur][(sub * 2 + g) * BNT + brw[cb]];                          \
+                        bsc[cb] = Scf[cur][(sub * 2 + g) * (BNT + 32) + brw[cb]];                   \
                 }                                                                                   \
                 _Pragma("unroll") for (int ks = 0; ks < BK / 16; ++ks)                              \
                 {                                                                                   \
@@ -292,23 +325,21 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
                     _Pragma("unroll") for (int ms = 0; ms < NMS; ++ms) af[ms] =                    \
                         frag_bf16(Asb, wm * WROWS + ms * 32 + (l & 31), kc);                        \
                     _Pragma("unroll") for (int cb = 0; cb < NCB; ++cb) bfr[cb] =                    \
-                        MX ? cvt_mx8(reinterpret_cast<const uint32_t *>(Bsb)[mx_slot(brw[cb], g) * 4 + ks], \
+                        MXL ? cvt_mx8(reinterpret_cast<const uint32_t *>(Bsb)[mx_slot(brw[cb], g) * 4 + ks], \
                                      bsc[cb])                                                       \
-                           : frag_bf16(Bsb, brw[cb], kc);                                           \
+                            : frag_bf16(Bsb, brw[cb], kc);                                          \
                     _Pragma("unroll") for (int ms = 0; ms < NMS; ++ms)                              \
                         _Pragma("unroll") for (int cb = 0; cb < NCB; ++cb) acc[ms][cb] =            \
                             __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ms], bfr[cb], acc[ms][cb], 0, 0, 0); \
                 }                                                                                   \
             }                                                                                       \
         }                                                                                           \
-        if ((KT) + 1 < nk)                                                                          \
-            sstore<MX, BNT, KS>(NXT, As[cur ^ 1], Bs[cur ^ 1], Scf[cur ^ 1], tid);                  \
+        sstore<MX, DQ, BNT, KS>(NXT, As[cur ^ 1], Bs[cur ^ 1], Scf[cur ^ 1], tid);                  \
         __syncthreads();                                                                            \
     }
         for (int kt = 0; kt < nk; kt += 2) {
             ECF_GEMM_BODY(kt, s1, s0)
-            if (kt + 1 < nk)
-                ECF_GEMM_BODY(kt + 1, s0, s1)
+            ECF_GEMM_BODY(kt + 1, s0, s1)
         }
 #undef ECF_GEMM_BODY
         // epilogue: a lane holds rows (j/4)*8 + (l/32)*4 + j%4 of column l%32 of each fragment
@@ -355,10 +386,13 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
 
 // ---------------------------------------------------------------------------------
 
-// Tile choice per weight format, measured on MI355X (C4 bf16 and C5 MXFP4
-// prefill layers): 128-weight-row N-tiles, two blocks per CU, one 64-wide
-// sub-tile per stage, 2 x 2 waves.  Wider tiles, two-sub-tile stages and a
-// 1 x 4 wave layout were each slower or spilled registers.
+// Tile choice per weight format, measured on MI355X (bf16: 4096-token layer,
+// d 4096, I 1024, top-6; MXFP4: 8192-token layer, I 2048, top-8): two blocks
+// per CU, one 64-wide sub-tile per stage, 2 x 2 waves; 128 weight rows per
+// N-tile for bf16 (HBM-bound there), 256 for MXFP4 (halves the A re-reads and
+// the per-row MFMA overheads).  Two-sub-tile stages, a 1 x 4 wave layout, three
+// blocks per CU and expanding MXFP4 to bf16 at the LDS store (DQ) were each
+// slower or spilled registers.
 #ifndef ECF_BF16_BNT
 #define ECF_BF16_BNT 128
 #define ECF_BF16_MINB 2
@@ -366,10 +400,13 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
 #define ECF_BF16_WM 2
 #endif
 #ifndef ECF_MX_BNT
-#define ECF_MX_BNT 128
+#define ECF_MX_BNT 256
 #define ECF_MX_MINB 2
 #define ECF_MX_KS 1
 #define ECF_MX_WM 2
+#endif
+#ifndef ECF_MX_DQ
+#define ECF_MX_DQ false
 #endif
 
 int launch_prefill_gemm1(const ecf_shape &s, const ExpertTables &ex, const RouteOut &o, const void *x,
@@ -381,11 +418,12 @@ int launch_prefill_gemm1(const ecf_shape &s, const ExpertTables &ex, const Route
     const int nblk = max_tiles(s, T) * NT;
     ProfScope p("prefill_gemm1", st);
 #define ECF_G1(MXV, BNV, MBV, KSV, WMV)                                                                    \
-    hipLaunchKernelGGL((k_grouped_gemm<1, MXV, BNV, MBV, KSV, WMV>), dim3(nblk), dim3(256), 0, st, ex.ptrs,  \
+    hipLaunchKernelGGL((k_grouped_gemm<1, MXV, BNV, MBV, KSV, WMV, (MXV) && ECF_MX_DQ>), dim3(nblk), dim3(256), 0, st, ex.ptrs,  \
                        ex.lay.off[0], ex.lay.off[1], ex.lay.off[3], ex.lay.off[4], o.tiles, o.n_tiles,         \
                        o.offsets, o.perm, (const uint16_t *)x, s.hidden, s.inter, s.hidden, s.top_k,         \
                        s.n_experts, T * s.top_k, NT, (void *)H)
-    // K = d; a stage of KS sub-tiles needs d % (64 * KS) == 0 (d is a multiple of 256)
+    // K = d; the main loop takes an even number of stages of KS sub-tiles: d % (128 * KS) == 0
+    // (d is a multiple of 256)
     if (mx)
         ECF_G1(true, ECF_MX_BNT, ECF_MX_MINB, ECF_MX_KS, ECF_MX_WM);
     else
@@ -404,18 +442,19 @@ int launch_prefill_gemm2(const ecf_shape &s, const ExpertTables &ex, const Route
     const int nblk = max_tiles(s, T) * NT;
     ProfScope p("prefill_gemm2", st);
 #define ECF_G2(MXV, BNV, MBV, KSV, WMV)                                                                    \
-    hipLaunchKernelGGL((k_grouped_gemm<2, MXV, BNV, MBV, KSV, WMV>), dim3(nblk), dim3(256), 0, st, ex.ptrs,  \
+    hipLaunchKernelGGL((k_grouped_gemm<2, MXV, BNV, MBV, KSV, WMV, (MXV) && ECF_MX_DQ>), dim3(nblk), dim3(256), 0, st, ex.ptrs,  \
                        ex.lay.off[2], ex.lay.off[2], ex.lay.off[5], ex.lay.off[5], o.tiles, o.n_tiles,         \
                        o.offsets, o.perm, H, s.inter, s.hidden, s.inter, s.top_k, s.n_experts, T * s.top_k,  \
                        NT, (void *)Y)
-    // K = I; two-sub-tile stages only when I % 128 == 0
+    // K = I; the main loop takes an even number of stages: two-sub-tile stages
+    // only when I % 256 == 0 (I % 128 == 0 holds on this path)
     if (mx) {
-        if (s.inter % (64 * ECF_MX_KS) == 0)
+        if (s.inter % (128 * ECF_MX_KS) == 0)
             ECF_G2(true, ECF_MX_BNT, ECF_MX_MINB, ECF_MX_KS, ECF_MX_WM);
         else
             ECF_G2(true, ECF_MX_BNT, ECF_MX_MINB, 1, ECF_MX_WM);
     } else {
-        if (s.inter % (64 * ECF_BF16_KS) == 0)
+        if (s.inter % (128 * ECF_BF16_KS) == 0)
             ECF_G2(false, ECF_BF16_BNT, ECF_BF16_MINB, ECF_BF16_KS, ECF_BF16_WM);
         else
             ECF_G2(false, ECF_BF16_BNT, ECF_BF16_MINB, 1, ECF_BF16_WM);
