@@ -11,7 +11,10 @@ Decode steps replay one captured HIP graph per batch.
 
 Alongside (`also`): decode at 1 and 4 tokens, bf16 prefill (4096 tokens), MXFP4
 prefill (8192 tokens, I 2048, top-8), the 43-layer cached decode with 37% slots
-and the q* split, and the prefill layer prefetch overlap.  `roofline` is for the
+and the q* split, the machine's B_P / B_H from ecf_bandwidth_profile, the
+cached-decode policy ablation at equal capacity (q* at the configured and at the
+measured ratio, every miss over PCIe, a static hot subset with every miss on the
+host), and the prefill layer prefetch overlap.  `roofline` is for the
 dominant kernel of the headline workload (decode gate/up GEMV); `cpu_baseline`
 is the oracle on a bounded sample of the headline workload.
 
@@ -324,7 +327,9 @@ def bench_prefetch(torch, ecf, syn, layers=4):
 
 # ---- cached decode (43 layers, 37% slots, q*) -------------------------------------------
 
-def bench_cached(torch, ecf, syn, T=16, steps=16, warmup=16, n_blobs=256):
+def cached_setup(torch, ecf, syn, T=16, steps=16, warmup=16, n_blobs=256):
+    """Host pool, device slots, activations and per-step router logits of the
+    43-layer cached-decode workload, shared by every policy run."""
     from expert_cache_ffn_amd.layer import Layer, pack_expert
     cfg = syn.CONFIGS["cached"]
     L, d, E, I, k = cfg.layers, cfg.hidden, cfg.experts, cfg.inter, cfg.top_k
@@ -343,24 +348,73 @@ def bench_cached(torch, ecf, syn, T=16, steps=16, warmup=16, n_blobs=256):
     del stage
     slots = torch.empty((n_slots, S), dtype=torch.uint8, device="cuda")
     hb = host.data_ptr()
-    pool = [hb + ((l * 97 + e) % n_blobs) * S for l in range(L) for e in range(E)]
-    cache = ecf.ecf_cache_create(L, E, n_slots, n_slots, S, slots.data_ptr(), pool, host_threads=0)
-    lay = Layer(shape, T)
-    cstream = torch.cuda.Stream()
-    xa = syn.activations(cfg, T, device="cuda")
-    res_f = torch.empty((T, d), dtype=torch.float32, device="cuda")
-    act = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    blob_of = lambda l, e: (l * 97 + e) % n_blobs
+    pool = [hb + blob_of(l, e) * S for l in range(L) for e in range(E)]
     n_logits = warmup + steps   # fresh routing every step: no replayed trace inflates the hit rate
     lgs = [[syn.router_logits(cfg, T, layer=l, step=s, device="cuda") for l in range(L)] for s in range(n_logits)]
+    torch.cuda.synchronize()  # setup queued on the default stream lands before the copy stream fills slots
+    return dict(cfg=cfg, shape=shape, S=S, L=L, E=E, T=T, d=d, n_slots=n_slots, host=host, slots=slots,
+                pool=pool, blob_of=blob_of, lgs=lgs, n_blobs=n_blobs, steps=steps, warmup=warmup,
+                layer=Layer(shape, T), cstream=torch.cuda.Stream(), xa=syn.activations(cfg, T, device="cuda"),
+                res_f=torch.empty((T, d), dtype=torch.float32, device="cuda"),
+                act=torch.empty((T, d), dtype=torch.bfloat16, device="cuda"))
+
+
+def static_hot_set(syn, cfg, n_slots):
+    """The n_slots most popular (layer, expert) pairs of the Zipf recipe: the same
+    top ranks in every layer (all layers share one popularity law), the
+    remainder spread one more rank over the first layers."""
+    L = cfg.layers
+    per, extra = divmod(n_slots, L)
+    hot = []
+    for l in range(L):
+        rank = syn.popularity_rank(cfg, l)
+        n_l = per + (1 if l < extra else 0)
+        hot.append(sorted(int(e) for e in (rank <= n_l).nonzero().flatten()))
+    return hot
+
+
+# cached-decode policies at equal capacity: (q mode, fixed or measured ratio, static hot set)
+POLICIES = {
+    "lru_qstar": "shared LRU, misses split by q* at the configured B_P/B_H = 0.4",
+    "lru_qstar_measured": "shared LRU, misses split by q* at the B_P/B_H measured by ecf_bandwidth_profile",
+    "lru_all_pcie": "shared LRU, every miss copied over PCIe (q = m)",
+    "static_hot": "the most popular pairs pinned once (static hot subset), every miss on the host (q = 0)",
+}
+
+
+def bench_cached(torch, ecf, syn, ctx, policy="lru_qstar", bw=None):
+    """One policy on the shared cached-decode setup; returns throughput and traffic."""
+    L, E, T, S = ctx["L"], ctx["E"], ctx["T"], ctx["S"]
+    steps, warmup, lgs, lay = ctx["steps"], ctx["warmup"], ctx["lgs"], ctx["layer"]
+    n_logits = len(lgs)
+    cache = ecf.ecf_cache_create(L, E, ctx["n_slots"], ctx["n_slots"], S, ctx["slots"].data_ptr(), ctx["pool"],
+                                 host_threads=0)
+    q_mode, b_p, b_h = ecf.ECF_Q_AUTO, 0.4, 1.0
+    if policy == "lru_qstar_measured":
+        b_p, b_h = bw["b_p_conc"], bw["b_h"]
+    elif policy == "lru_all_pcie":
+        q_mode = ecf.ECF_Q_ALL_GPU
+    elif policy == "static_hot":
+        q_mode = ecf.ECF_Q_ALL_HOST
+        for l, hot in enumerate(static_hot_set(syn, ctx["cfg"], ctx["n_slots"])):
+            ecf.expert_cache_lookup(cache, l, hot)
+            slots, _ = ecf.expert_cache_evict(cache, l, hot)
+            for e, sl in zip(hot, slots):
+                ctx["slots"][sl].copy_(ctx["host"][ctx["blob_of"](l, e)], non_blocking=True)
+        torch.cuda.synchronize()
+    elif policy != "lru_qstar":
+        raise ValueError(policy)
     totals = dict(unique=0, hits=0, misses=0, q=0, host=0, h2d=0, hostb=0, wait=0.0, hostms=0.0)
     qhist = {}
+    res_f, act, xa = ctx["res_f"], ctx["act"], ctx["xa"]
 
     def one_step(s, record):
         x = xa
         res_f.zero_()
         for l in range(L):
-            a = lay.args(layer=l, router_logits=lgs[s % n_logits][l], cache=cache, b_p=0.4, b_h=1.0,
-                         copy_stream=cstream, residual=res_f, out_act=act)
+            a = lay.args(layer=l, router_logits=lgs[s % n_logits][l], cache=cache, b_p=b_p, b_h=b_h,
+                         q_mode=q_mode, copy_stream=ctx["cstream"], residual=res_f, out_act=act)
             st = lay.forward(a, x, res_f)
             x = act
             if record:
@@ -375,7 +429,7 @@ def bench_cached(torch, ecf, syn, T=16, steps=16, warmup=16, n_blobs=256):
                 totals["hostms"] += st["ms_host_ffn"]
                 qhist[st["q"]] = qhist.get(st["q"], 0) + 1
 
-    torch.cuda.synchronize()  # setup queued on the default stream lands before the copy stream fills slots
+    torch.cuda.synchronize()
     st0 = ecf.ecf_cache_get_stats(cache)
     for s in range(warmup):
         one_step(s, False)
@@ -390,19 +444,36 @@ def bench_cached(torch, ecf, syn, T=16, steps=16, warmup=16, n_blobs=256):
     ecf.ecf_cache_destroy(cache)
     miss_cold = (st1["misses"] - st0["misses"]) / max(1, st1["lookups"] - st0["lookups"])
     miss_steady = (st2["misses"] - st1["misses"]) / max(1, st2["lookups"] - st1["lookups"])
-    res = dict(tokens=T, layers=L, slots=n_slots, steps=steps, warmup=warmup, ms_per_step=1e3 * el / steps,
-               tokens_per_s=T * steps / el, miss_rate_steady=miss_steady, miss_rate_warmup=miss_cold,
-               unique_per_layer=totals["unique"] / (steps * L), q_total=totals["q"], host_total=totals["host"],
+    res = dict(policy=policy, policy_desc=POLICIES[policy], b_p=b_p, b_h=b_h,
+               tokens=T, layers=L, slots=ctx["n_slots"], steps=steps, warmup=warmup,
+               ms_per_step=1e3 * el / steps, tokens_per_s=T * steps / el, miss_rate_steady=miss_steady,
+               miss_rate_warmup=miss_cold, unique_per_layer=totals["unique"] / (steps * L),
+               q_total=totals["q"], host_total=totals["host"],
                pcie_GBps=totals["h2d"] / el / 1e9, host_read_GBps=totals["hostb"] / el / 1e9,
                ms_wait_route_per_step=totals["wait"] / steps, ms_host_ffn_per_step=totals["hostms"] / steps,
-               q_hist={str(q): n for q, n in sorted(qhist.items())}, host_blobs=n_blobs,
+               q_hist={str(q): n for q, n in sorted(qhist.items())}, host_blobs=ctx["n_blobs"],
                host_threads="default (min(16, hardware threads))")
-    log(f"cached: {res['ms_per_step']:.1f} ms/step ({L} layers), {res['tokens_per_s']:.1f} tok/s, "
+    log(f"cached [{policy}]: {res['ms_per_step']:.1f} ms/step ({L} layers), {res['tokens_per_s']:.1f} tok/s, "
         f"steady miss rate {100 * miss_steady:.1f}%, PCIe {res['pcie_GBps']:.1f} GB/s, "
         f"host {res['host_read_GBps']:.1f} GB/s")
-    del slots, host
-    torch.cuda.empty_cache()
     return res
+
+
+def bench_bandwidth(torch, ecf, ctx, seconds=2.0):
+    """ecf_bandwidth_profile on 16 blobs of the cached pool (the q* inputs)."""
+    S = ctx["S"]
+    n = min(16, ctx["n_blobs"])
+    dbuf = torch.empty((4, S), dtype=torch.uint8, device="cuda")
+    cs = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    r = ecf.ecf_bandwidth_profile(ctx["shape"], [ctx["host"].data_ptr() + i * S for i in range(n)],
+                                  dbuf.data_ptr(), dbuf.numel(), copy_stream=cs.cuda_stream, seconds=seconds)
+    del dbuf
+    r["ratio_b_p_over_b_h"] = r["b_p_conc"] / r["b_h"]
+    log(f"bandwidth: B_P {r['b_p']:.1f} GB/s alone, {r['b_p_conc']:.1f} with host experts; host experts "
+        f"{r['b_cpu']:.1f} alone, {r['b_cpu_conc']:.1f} with copies ({r['host_threads']} threads); plain read "
+        f"{r['b_read']:.1f}; B_H = {r['b_h']:.1f} GB/s, B_P/B_H = {r['ratio_b_p_over_b_h']:.3f}")
+    return r
 
 
 # ---- main ----------------------------------------------------------------------------------------
@@ -412,7 +483,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workloads", default="decode,prefill,prefill_fp4,prefetch,cached")
+    ap.add_argument("--workloads", default="decode,prefill,prefill_fp4,prefetch,cached,bandwidth,policies",
+                    help="any of decode, prefill, prefill_fp4, prefetch, cached, bandwidth, policies "
+                         "(policies: the cached-decode policy ablation at equal capacity)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--cached-steps", type=int, default=12)
@@ -465,9 +538,21 @@ def main():
     torch.cuda.empty_cache()
     if "prefetch" in wl:
         also["prefill_prefetch_stack"] = bench_prefetch(torch, ecf, syn)
-    if "cached" in wl:
-        also["cached_decode_43L_T16"] = bench_cached(torch, ecf, syn, steps=args.cached_steps,
-                                                     warmup=args.cached_steps)
+    if wl & {"cached", "bandwidth", "policies"}:
+        ctx = cached_setup(torch, ecf, syn, steps=args.cached_steps, warmup=args.cached_steps)
+        bw = None
+        if wl & {"bandwidth", "policies"}:
+            bw = also["bandwidth_profile"] = bench_bandwidth(torch, ecf, ctx)
+        if "cached" in wl:
+            also["cached_decode_43L_T16"] = bench_cached(torch, ecf, syn, ctx, "lru_qstar")
+        if "policies" in wl:
+            pol = {p: (dict(also["cached_decode_43L_T16"]) if p == "lru_qstar" and "cached" in wl
+                       else bench_cached(torch, ecf, syn, ctx, p, bw)) for p in POLICIES}
+            for r in pol.values():
+                r.pop("q_hist")
+            also["cached_policies_43L_T16"] = pol
+        del ctx
+        torch.cuda.empty_cache()
     if head is None:  # a partial run (profiling): no headline line
         print(json.dumps({"partial": True, "also": also}), flush=True)
         return

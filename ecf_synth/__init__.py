@@ -13,6 +13,7 @@ and hands the same bytes to both sides.
 """
 from .gen import (  # noqa: F401
     CONFIGS,
+    Config,
     T_X, T_WR, T_WG, T_WU, T_WD, T_LOGITS, T_PERM,
     key_of,
     uniform,
@@ -24,4 +25,5 @@ from .gen import (  # noqa: F401
     activations,
     router_logits,
     zipf_gumbel_logits,
+    popularity_rank,
 )

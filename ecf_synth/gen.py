@@ -193,6 +193,15 @@ def expert_weights(cfg: Config, layer: int, expert: int, device="cpu", dtype=Non
     return out
 
 
+def popularity_rank(cfg: Config, layer: int, device="cpu") -> torch.Tensor:
+    """Rank (1 = most popular) of each expert of `layer` in the Zipf recipe, fp64 [E]."""
+    E = cfg.experts
+    u = uniform(key_of(cfg.cid, layer, T_PERM), E, device)
+    rank = torch.empty(E, dtype=torch.float64, device=device)
+    rank[torch.argsort(u, stable=True)] = torch.arange(1, E + 1, dtype=torch.float64, device=device)
+    return rank
+
+
 def zipf_gumbel_logits(cfg: Config, layer: int, step: int, T: int, device="cpu"):
     """Logits whose top-k is a Zipf(s)-weighted draw without replacement.
 
@@ -203,9 +212,7 @@ def zipf_gumbel_logits(cfg: Config, layer: int, step: int, T: int, device="cpu")
     (the Gumbel-top-k construction of Kool, van Hoof and Welling, ICML 2019).
     """
     E = cfg.experts
-    u = uniform(key_of(cfg.cid, layer, T_PERM), E, device)
-    rank = torch.empty(E, dtype=torch.float64, device=device)
-    rank[torch.argsort(u, stable=True)] = torch.arange(1, E + 1, dtype=torch.float64, device=device)
+    rank = popularity_rank(cfg, layer, device)
     logp = -cfg.zipf_s * torch.log(rank)
     logp = logp - torch.logsumexp(logp, 0)
     g = uniform(key_of(cfg.cid, layer, T_LOGITS, 0, step), T * E, device).view(T, E)

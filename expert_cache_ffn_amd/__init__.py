@@ -13,11 +13,11 @@ from ._lib import (  # noqa: F401
     ECF_F32, ECF_BF16, ECF_MXFP4,
     ECF_Q_AUTO, ECF_Q_ALL_GPU, ECF_Q_ALL_HOST, ECF_Q_FIXED,
     ECF_PATH_AUTO, ECF_PATH_DECODE, ECF_PATH_PREFILL,
-    EcfError, Shape, LayerArgs, StepStats, CacheStats, EXPORTS,
+    EcfError, Shape, LayerArgs, StepStats, CacheStats, BwProfile, EXPORTS,
     lib, make_shape,
     ecf_expert_bytes, ecf_expert_layout, ecf_workspace_bytes, qstar_split,
     ecf_cache_create, ecf_cache_destroy, expert_cache_lookup, expert_cache_evict,
     ecf_cache_available, ecf_cache_slot_of, ecf_cache_get_stats, ecf_cache_resize,
-    prefetch_layer, moe_layer_forward, ecf_host_experts,
+    prefetch_layer, moe_layer_forward, ecf_host_experts, ecf_bandwidth_profile,
     ecf_profile_enable, ecf_profile_get_all, ecf_profile_reset,
 )

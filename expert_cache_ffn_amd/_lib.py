@@ -24,8 +24,8 @@ EXPORTS = [
     "ecf_last_error", "ecf_expert_bytes", "ecf_expert_layout", "ecf_workspace_bytes", "qstar_split",
     "ecf_cache_create", "ecf_cache_destroy", "expert_cache_lookup", "expert_cache_evict",
     "ecf_cache_available", "ecf_cache_slot_of", "ecf_cache_get_stats", "ecf_cache_resize",
-    "prefetch_layer", "moe_layer_forward", "ecf_host_experts", "ecf_profile_enable", "ecf_profile_get",
-    "ecf_profile_reset",
+    "prefetch_layer", "moe_layer_forward", "ecf_host_experts", "ecf_bandwidth_profile", "ecf_profile_enable",
+    "ecf_profile_get", "ecf_profile_reset",
 ]
 
 
@@ -51,6 +51,14 @@ class StepStats(Structure):
     _fields_ = [("n_unique", c_int32), ("hits", c_int32), ("misses", c_int32), ("q", c_int32),
                 ("host", c_int32), ("path", c_int32), ("bytes_h2d", c_int64), ("bytes_host", c_int64),
                 ("ms_wait_route", c_double), ("ms_host_ffn", c_double)]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class BwProfile(Structure):
+    _fields_ = [(n, c_double) for n in ("b_p", "b_cpu", "b_read", "b_p_conc", "b_cpu_conc", "b_h")] + \
+        [("host_threads", c_int32)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -105,6 +113,9 @@ def lib():
         L.ecf_host_experts.argtypes = [POINTER(Shape), c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                                        c_void_p, c_int32]
         L.ecf_host_experts.restype = c_int32
+        L.ecf_bandwidth_profile.argtypes = [POINTER(Shape), c_int32, c_void_p, c_int32, c_void_p, c_size_t,
+                                            c_void_p, c_double, POINTER(BwProfile)]
+        L.ecf_bandwidth_profile.restype = c_int32
         L.ecf_profile_enable.argtypes, L.ecf_profile_enable.restype = [c_int32], c_int32
         L.ecf_profile_get.argtypes = [c_int32, POINTER(c_char_p), POINTER(c_int64), POINTER(c_double)]
         L.ecf_profile_get.restype = c_int32
@@ -227,6 +238,16 @@ def ecf_host_experts(shape: Shape, blob_ptrs, rows_per_job, x_ptr, n_tokens, y_p
     flat, _ = _i32([f for r in rows_per_job for f in r])
     _check(lib().ecf_host_experts(ctypes.byref(shape), n, blobs, counts, flat, c_void_p(int(x_ptr)),
                                   int(n_tokens), c_void_p(int(y_ptr)), int(n_threads)))
+
+
+def ecf_bandwidth_profile(shape: Shape, blob_ptrs, d_buf, d_buf_bytes, copy_stream=0, seconds=2.0,
+                          host_threads=0) -> dict:
+    arr = (c_void_p * max(1, len(blob_ptrs)))(*[int(p) for p in blob_ptrs])
+    out = BwProfile()
+    _check(lib().ecf_bandwidth_profile(ctypes.byref(shape), len(blob_ptrs), arr, int(host_threads),
+                                       int(d_buf) or None, int(d_buf_bytes), int(copy_stream) or None,
+                                       float(seconds), ctypes.byref(out)))
+    return out.as_dict()
 
 
 def ecf_profile_enable(on: bool):

@@ -12,7 +12,7 @@ OUT = os.path.join(HERE, "libecf.so")
 BUILD = os.path.join(os.path.dirname(HERE), "_build")
 
 HIP_SRCS = ["k_route.hip", "k_decode.hip", "k_prefill.hip"]
-CPP_SRCS = ["api.cpp", "cache.cpp", "qstar.cpp", "host_ffn.cpp"]
+CPP_SRCS = ["api.cpp", "cache.cpp", "qstar.cpp", "host_ffn.cpp", "bwprof.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -245,6 +245,34 @@ int ecf_host_experts(const ecf_shape *shape, int32_t n_jobs, const void *const *
                      const int32_t *n_rows, const int32_t *rows, const void *h_x, int32_t n_tokens,
                      float *h_y, int32_t n_threads);
 
+/* ---- bandwidth profiler for the split [TF "FreeToken's three core mechanisms" /
+ *      "Bandwidth-adaptive execution (q* policy)": the split ratio is measured on
+ *      the machine the engine runs on] -----------------------------------------------
+ * Measures, for about `seconds` in total:
+ *   b_p         pinned host -> device copies of whole expert blobs on copy_stream
+ *               (NULL = the null stream), alone;
+ *   b_cpu       expert weight bytes per second the host expert threads consume
+ *               (the forward pass's own host FFN, one routed row per expert), alone;
+ *   b_read      a plain streaming read of the blobs by the same threads;
+ *   b_p_conc, b_cpu_conc   the copy and host-expert rates while both run;
+ *   b_h         b_p_conc + b_cpu_conc: the host bandwidth the two share.
+ * All in GB/s (1e9 B/s).  Pass (b_p_conc, b_h) as (b_p, b_h) to qstar_split or
+ * ecf_layer_args.  h_blobs: n_blobs pinned host expert blobs of `shape` (fp32 or
+ * bf16 weights; MXFP4 -> ECF_EUNSUPPORTED), read only.  d_buf: device scratch of
+ * d_buf_bytes >= one blob (ECF_ENOSPC otherwise), overwritten.  host_threads 0 =
+ * min(16, hardware threads).  Allocates its thread pool; blocks until done.
+ * ECF_EINVAL for NULL pointers, n_blobs < 1 or seconds <= 0; ECF_EHIP on a HIP
+ * failure.
+ */
+typedef struct {
+    double b_p, b_cpu, b_read, b_p_conc, b_cpu_conc, b_h;
+    int32_t host_threads;
+} ecf_bw_profile;
+
+int ecf_bandwidth_profile(const ecf_shape *shape, int32_t n_blobs, const void *const *h_blobs,
+                          int32_t host_threads, void *d_buf, size_t d_buf_bytes, void *copy_stream,
+                          double seconds, ecf_bw_profile *out);
+
 /* ---- measurement hooks ------------------------------------------------------------- */
 /* When enabled, every kernel launch is bracketed by HIP events on its stream
  * and its duration is accumulated per kernel name (adds event overhead). */

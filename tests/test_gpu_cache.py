@@ -181,3 +181,26 @@ def test_prefetch_layer_copies_and_signals():
     with pytest.raises(ecf.EcfError) as ei:
         ecf.prefetch_layer(h.data_ptr(), dbuf.data_ptr(), n, n - 1, s.cuda_stream, ev.cuda_event)
     assert ei.value.code == ecf.ECF_ENOSPC
+
+
+def test_bandwidth_profile_sane():
+    """ecf_bandwidth_profile on a few small pinned blobs: every rate positive,
+    b_h the sum of the concurrent rates, and its ratio usable by qstar_split."""
+    cfg = syn.Config(90, "bw", (1,), 1024, 8, 512, 2, "bf16", "bf16", "router")
+    shape = shape_of(cfg)
+    S = ecf.ecf_expert_bytes(shape)
+    n = 6
+    host = torch.zeros((n, S), dtype=torch.uint8).pin_memory()
+    dbuf = torch.empty((4, S), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    say(f"bandwidth profile: {n} blobs of {S} bytes, 0.4 s")
+    r = ecf.ecf_bandwidth_profile(shape, [host.data_ptr() + i * S for i in range(n)], dbuf.data_ptr(),
+                                  dbuf.numel(), seconds=0.4, host_threads=4)
+    say(str(r))
+    for key in ("b_p", "b_cpu", "b_read", "b_p_conc", "b_cpu_conc", "b_h"):
+        assert r[key] > 0.0 and np.isfinite(r[key]), key
+    assert r["b_h"] == pytest.approx(r["b_p_conc"] + r["b_cpu_conc"], rel=1e-12)
+    assert r["host_threads"] == 4
+    for m in (0, 1, 7, 40):
+        q = ecf.qstar_split(m, r["b_p_conc"], r["b_h"])
+        assert 0 <= q <= m

@@ -224,3 +224,26 @@ def test_host_experts_against_oracle(w_dtype):
             ref[f] = oracle.expert_ffn(experts[e], x64[f // k], w_dtype)
     rms = np.sqrt(np.mean(ref ** 2))
     assert np.max(np.abs(y.numpy() - ref)) <= 1e-5 * rms
+
+
+def test_bandwidth_profile_argument_checks():
+    """Every rejection happens before any HIP call (fake pointers are never used)."""
+    bf = ecf.make_shape(1024, 512, 8, 2, "bf16", "bf16")
+    S = ecf.ecf_expert_bytes(bf)
+    fake = [4096, 8192]
+
+    def code(**kw):
+        a = dict(shape=bf, blob_ptrs=fake, d_buf=4096, d_buf_bytes=4 * S, seconds=0.5)
+        a.update(kw)
+        with pytest.raises(ecf.EcfError) as ei:
+            ecf.ecf_bandwidth_profile(**a)
+        return ei.value.code
+
+    assert code(blob_ptrs=[]) == ecf.ECF_EINVAL
+    assert code(blob_ptrs=[4096, 0]) == ecf.ECF_EINVAL
+    assert code(d_buf=0) == ecf.ECF_EINVAL
+    assert code(seconds=0.0) == ecf.ECF_EINVAL
+    assert code(host_threads=-1) == ecf.ECF_EINVAL
+    assert code(d_buf_bytes=S - 1) == ecf.ECF_ENOSPC
+    assert code(shape=ecf.make_shape(1024, 512, 8, 2, "mxfp4", "bf16")) == ecf.ECF_EUNSUPPORTED
+    assert code(shape=ecf.make_shape(1000, 512, 8, 2, "bf16", "bf16")) == ecf.ECF_EINVAL
