@@ -52,12 +52,16 @@ def src_hash(*names):
 
 # ---- decode (headline) ---------------------------------------------------------------
 
-def bench_decode(torch, ecf, syn, Ts, steps, warmup, n_batches=64, use_graph=True, host_inputs=False):
+def bench_decode(torch, ecf, syn, Ts, steps, warmup, n_batches=64, use_graph=True, host_inputs=False,
+                 w_dtype="bf16"):
+    import dataclasses
     from expert_cache_ffn_amd.layer import ExpertPool, Layer, pack_expert
-    cfg = syn.CONFIGS["decode"]
+    cfg = dataclasses.replace(syn.CONFIGS["decode"], w_dtype=w_dtype)
     d, E, I, k = cfg.hidden, cfg.experts, cfg.inter, cfg.top_k
-    shape = ecf.make_shape(d, I, E, k, "bf16", "bf16")
+    shape = ecf.make_shape(d, I, E, k, w_dtype, "bf16")
     S = ecf.ecf_expert_bytes(shape)
+    # gate + up bytes of one expert: the two weight sections (+ their scales for MXFP4)
+    gu_expert = 2 * (I * d * 2 if w_dtype == "bf16" else I * d // 2 + I * d // 32)
     pool = ExpertPool(shape, "cuda")
     # host_inputs: every input is generated on the host and copied, so the only
     # GPU kernels of the run are libecf's and the runtime's copies (a hardware
@@ -138,7 +142,7 @@ def bench_decode(torch, ecf, syn, Ts, steps, warmup, n_batches=64, use_graph=Tru
         used = [i % n_batches for i in range(steps)]
         U_avg = float(U[used].mean())
         R = T * k
-        gu_bytes = U_avg * 2 * I * d * 2 + R * d * 2 + R * I * 4       # gate+up weights, x rows, h
+        gu_bytes = U_avg * gu_expert + R * d * 2 + R * I * 4           # gate+up weights, x rows, h
         layer_bytes = U_avg * S + E * d * 2 + T * d * 2 + T * d * 4    # weights, router, x, out
         kern = {n: {"launches": c, "avg_us": 1e3 * t / max(c, 1)} for n, (c, t) in prof.items()}
         gu_us = kern["decode_gateup"]["avg_us"]
@@ -148,7 +152,7 @@ def bench_decode(torch, ecf, syn, Ts, steps, warmup, n_batches=64, use_graph=Tru
             layer_hbm_frac=layer_bytes / (ms / steps * 1e-3) / 1e9 / HBM_PEAK_GBS,
             gateup_bytes=gu_bytes, gateup_avg_us=gu_us, gateup_GBps=gu_bytes / (gu_us * 1e-6) / 1e9,
             kernels=kern, graph=use_graph)
-        log(f"decode T={T}: {ms / steps * 1e3:.1f} us/step, {results[T]['tokens_per_s']:.0f} tok/s, "
+        log(f"decode {w_dtype} T={T}: {ms / steps * 1e3:.1f} us/step, {results[T]['tokens_per_s']:.0f} tok/s, "
             f"U={U_avg:.1f}, layer {results[T]['layer_GBps']:.0f} GB/s, gate/up {results[T]['gateup_GBps']:.0f} GB/s")
         del graphs
     sample = dict(pool=pool, wr=wr, cfg=cfg)
@@ -327,16 +331,17 @@ def bench_prefetch(torch, ecf, syn, layers=4):
 
 # ---- cached decode (43 layers, 37% slots, q*) -------------------------------------------
 
-def cached_setup(torch, ecf, syn, T=16, steps=16, warmup=16, n_blobs=256):
+def cached_setup(torch, ecf, syn, T=16, steps=16, warmup=16, n_blobs=256, w_dtype="bf16"):
     """Host pool, device slots, activations and per-step router logits of the
     43-layer cached-decode workload, shared by every policy run."""
+    import dataclasses
     from expert_cache_ffn_amd.layer import Layer, pack_expert
-    cfg = syn.CONFIGS["cached"]
+    cfg = dataclasses.replace(syn.CONFIGS["cached"], w_dtype=w_dtype)
     L, d, E, I, k = cfg.layers, cfg.hidden, cfg.experts, cfg.inter, cfg.top_k
-    shape = ecf.make_shape(d, I, E, k, "bf16", "bf16")
+    shape = ecf.make_shape(d, I, E, k, w_dtype, "bf16")
     S = ecf.ecf_expert_bytes(shape)
     n_slots = int(0.37 * L * E)
-    log(f"cached: {L} layers x {E} experts, {n_slots} slots ({n_slots * S / 1e9:.1f} GB HBM), "
+    log(f"cached {w_dtype}: {L} layers x {E} experts, {n_slots} slots ({n_slots * S / 1e9:.1f} GB HBM), "
         f"host pool of {n_blobs} distinct blobs ({n_blobs * S / 1e9:.1f} GB pinned) aliased over layers")
     host = torch.empty((n_blobs, S), dtype=torch.uint8).pin_memory()
     stage = torch.empty((16, S), dtype=torch.uint8, device="cuda")
@@ -353,7 +358,7 @@ def cached_setup(torch, ecf, syn, T=16, steps=16, warmup=16, n_blobs=256):
     n_logits = warmup + steps   # fresh routing every step: no replayed trace inflates the hit rate
     lgs = [[syn.router_logits(cfg, T, layer=l, step=s, device="cuda") for l in range(L)] for s in range(n_logits)]
     torch.cuda.synchronize()  # setup queued on the default stream lands before the copy stream fills slots
-    return dict(cfg=cfg, shape=shape, S=S, L=L, E=E, T=T, d=d, n_slots=n_slots, host=host, slots=slots,
+    return dict(cfg=cfg, shape=shape, S=S, L=L, E=E, T=T, d=d, n_slots=n_slots, host=host, slots=slots, w_dtype=w_dtype,
                 pool=pool, blob_of=blob_of, lgs=lgs, n_blobs=n_blobs, steps=steps, warmup=warmup,
                 layer=Layer(shape, T), cstream=torch.cuda.Stream(), xa=syn.activations(cfg, T, device="cuda"),
                 res_f=torch.empty((T, d), dtype=torch.float32, device="cuda"),
@@ -444,7 +449,7 @@ def bench_cached(torch, ecf, syn, ctx, policy="lru_qstar", bw=None):
     ecf.ecf_cache_destroy(cache)
     miss_cold = (st1["misses"] - st0["misses"]) / max(1, st1["lookups"] - st0["lookups"])
     miss_steady = (st2["misses"] - st1["misses"]) / max(1, st2["lookups"] - st1["lookups"])
-    res = dict(policy=policy, policy_desc=POLICIES[policy], b_p=b_p, b_h=b_h,
+    res = dict(policy=policy, policy_desc=POLICIES[policy], w_dtype=ctx["w_dtype"], slot_bytes=S, b_p=b_p, b_h=b_h,
                tokens=T, layers=L, slots=ctx["n_slots"], steps=steps, warmup=warmup,
                ms_per_step=1e3 * el / steps, tokens_per_s=T * steps / el, miss_rate_steady=miss_steady,
                miss_rate_warmup=miss_cold, unique_per_layer=totals["unique"] / (steps * L),
@@ -453,7 +458,7 @@ def bench_cached(torch, ecf, syn, ctx, policy="lru_qstar", bw=None):
                ms_wait_route_per_step=totals["wait"] / steps, ms_host_ffn_per_step=totals["hostms"] / steps,
                q_hist={str(q): n for q, n in sorted(qhist.items())}, host_blobs=ctx["n_blobs"],
                host_threads="default (min(16, hardware threads))")
-    log(f"cached [{policy}]: {res['ms_per_step']:.1f} ms/step ({L} layers), {res['tokens_per_s']:.1f} tok/s, "
+    log(f"cached {ctx['w_dtype']} [{policy}]: {res['ms_per_step']:.1f} ms/step ({L} layers), {res['tokens_per_s']:.1f} tok/s, "
         f"steady miss rate {100 * miss_steady:.1f}%, PCIe {res['pcie_GBps']:.1f} GB/s, "
         f"host {res['host_read_GBps']:.1f} GB/s")
     return res
@@ -483,9 +488,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workloads", default="decode,prefill,prefill_fp4,prefetch,cached,bandwidth,policies",
-                    help="any of decode, prefill, prefill_fp4, prefetch, cached, bandwidth, policies "
-                         "(policies: the cached-decode policy ablation at equal capacity)")
+    ap.add_argument("--workloads",
+                    default="decode,decode_fp4,prefill,prefill_fp4,prefetch,cached,bandwidth,policies,cached_fp4",
+                    help="any of decode, decode_fp4, prefill, prefill_fp4, prefetch, cached, bandwidth, policies, "
+                         "cached_fp4 (policies: the cached-decode policy ablation at equal capacity; *_fp4: the "
+                         "same layers with MXFP4 experts)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--cached-steps", type=int, default=12)
@@ -524,6 +531,11 @@ def main():
                                    host_inputs=args.host_inputs)
         head = dec.get(16)
         also.update({f"decode_T{T}": dec[T] for T in Ts if T != 16})
+    if "decode_fp4" in wl:
+        dec4, _ = bench_decode(torch, ecf, syn, (1, 16), args.steps, args.warmup, use_graph=not args.no_graph,
+                               host_inputs=args.host_inputs, w_dtype="mxfp4")
+        also.update({f"decode_mxfp4_T{T}": dec4[T] for T in dec4})
+        torch.cuda.empty_cache()
     if "prefill" in wl:
         also["prefill_bf16_T4096"] = bench_prefill(torch, ecf, syn, "prefill", max(5, args.steps // 20),
                                                    max(2, args.warmup // 5))
@@ -551,6 +563,15 @@ def main():
             for r in pol.values():
                 r.pop("q_hist")
             also["cached_policies_43L_T16"] = pol
+        del ctx
+        torch.cuda.empty_cache()
+    if "cached_fp4" in wl:
+        ctx = cached_setup(torch, ecf, syn, steps=args.cached_steps, warmup=args.cached_steps, w_dtype="mxfp4")
+        bw4 = also["bandwidth_profile_mxfp4"] = bench_bandwidth(torch, ecf, ctx)
+        for p in ("lru_qstar", "lru_qstar_measured"):
+            r = bench_cached(torch, ecf, syn, ctx, p, bw4)
+            r.pop("q_hist")
+            also[f"cached_decode_mxfp4_43L_T16_{p}"] = r
         del ctx
         torch.cuda.empty_cache()
     if head is None:  # a partial run (profiling): no headline line

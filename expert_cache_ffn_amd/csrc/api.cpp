@@ -342,8 +342,7 @@ static int pick_path(const ecf_layer_args *a, int32_t T)
         return a->path;
     if (a->shape.w_dtype == ECF_F32)
         return ECF_PATH_DECODE;
-    if (a->shape.w_dtype == ECF_MXFP4)
-        return ECF_PATH_PREFILL;
+    // bf16 and MXFP4: GEMV while each expert sees a few rows, grouped GEMM beyond
     return (T <= 64 || a->shape.inter % 128) ? ECF_PATH_DECODE : ECF_PATH_PREFILL;
 }
 
@@ -535,6 +534,8 @@ int moe_layer_forward(const ecf_layer_args *a, const void *d_x, int32_t T, float
             return set_error(ECF_EINVAL, "give exactly one of d_expert_ptrs and cache");
         if ((uintptr_t)a->d_ws % 256)
             return set_error(ECF_EINVAL, "workspace must be 256-byte aligned");
+        if ((uintptr_t)d_x % 16)
+            return set_error(ECF_EINVAL, "x must be 16-byte aligned");
         const WsLayout wl = ws_layout(s, T);
         if (a->ws_bytes < wl.total)
             return set_error(ECF_ENOSPC, "workspace too small: %zu < %zu bytes for %d tokens", a->ws_bytes,
@@ -542,8 +543,6 @@ int moe_layer_forward(const ecf_layer_args *a, const void *d_x, int32_t T, float
         const int path = pick_path(a, T);
         if (path == ECF_PATH_PREFILL && (s.w_dtype == ECF_F32 || s.inter % 128))
             return set_error(ECF_EUNSUPPORTED, "the prefill path needs bf16/MXFP4 weights and inter %% 128 == 0");
-        if (path == ECF_PATH_DECODE && s.w_dtype == ECF_MXFP4)
-            return set_error(ECF_EUNSUPPORTED, "MXFP4 weights run on the prefill path");
         hipStream_t stream = (hipStream_t)a->stream;
         char *ws = (char *)a->d_ws;
         BlobLayout lay;

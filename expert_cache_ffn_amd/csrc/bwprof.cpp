@@ -126,8 +126,6 @@ extern "C" int ecf_bandwidth_profile(const ecf_shape *shape, int32_t n_blobs, co
         const size_t S = ecf_expert_bytes(shape);
         if (S == 0)
             return ECF_EINVAL;  // ecf_expert_bytes set the message
-        if (shape->w_dtype == ECF_MXFP4)
-            return set_error(ECF_EUNSUPPORTED, "ecf_bandwidth_profile: host experts take fp32 or bf16 weights");
         blob_layout(*shape, &lay);
         if (d_buf_bytes < S)
             return set_error(ECF_ENOSPC, "ecf_bandwidth_profile: device buffer %zu B < one expert (%zu B)",

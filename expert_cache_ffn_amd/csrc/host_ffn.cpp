@@ -98,17 +98,40 @@ inline float bf_to_f(uint16_t b)
     return f;
 }
 
+// Weight formats of a row: fp32, bf16, or MXFP4 (OCP MX v1.0: E2M1 elements,
+// element 2i in the low nibble of byte i, one E8M0 scale per 32 elements).
+enum { HF_F32 = 0, HF_BF16 = 1, HF_MX = 2 };
+
+constexpr float kE2M1[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+
+inline float e8m0(uint8_t s)
+{
+    return s == 0 ? std::ldexp(1.0f, -127) : std::ldexp(1.0f, (int)s - 127);
+}
+
+// Weight c of a row (scalar build).
+template <int WF>
+inline float wval(const void *w, const uint8_t *sc, int c)
+{
+    if (WF == HF_BF16)
+        return bf_to_f(((const uint16_t *)w)[c]);
+    if (WF == HF_F32)
+        return ((const float *)w)[c];
+    const uint8_t b = ((const uint8_t *)w)[c >> 1];
+    const int code = (c & 1) ? b >> 4 : b & 15;
+    const float v = kE2M1[code & 7] * e8m0(sc[c >> 5]);
+    return (code & 8) ? -v : v;
+}
+
 // out[r] = sum_c w[c] * xs[r][c], 16 partial sums per row (scalar build).
-template <bool WBF>
-void dots_scalar(const void *w, const float *const *xs, int nr, int n, float *out)
+template <int WF>
+void dots_scalar(const void *w, const uint8_t *sc, const float *const *xs, int nr, int n, float *out)
 {
     for (int r = 0; r < nr; ++r) {
         float acc[16] = {};
         for (int c = 0; c < n; c += 16)
-            for (int i = 0; i < 16; ++i) {
-                const float wv = WBF ? bf_to_f(((const uint16_t *)w)[c + i]) : ((const float *)w)[c + i];
-                acc[i] += wv * xs[r][c + i];
-            }
+            for (int i = 0; i < 16; ++i)
+                acc[i] += wval<WF>(w, sc, c + i) * xs[r][c + i];
         float s = 0.f;
         for (int i = 0; i < 16; ++i)
             s += acc[i];
@@ -125,31 +148,51 @@ __attribute__((target("avx2,fma"))) inline float hsum256(__m256 v)
     return _mm_cvtss_f32(lo);
 }
 
-// Same sums with AVX2: two 8-wide accumulators per row = 16 partial sums.
-template <bool WBF>
-__attribute__((target("avx2,fma"))) void dots_avx2(const void *w, const float *const *xs, int nr, int n,
-                                                   float *out)
+// 8 E2M1 codes (int32 lanes) -> fp32 values times the block scale (exact).
+__attribute__((target("avx2,fma"))) inline __m256 e2m1x8(__m256i code, __m256 scale)
 {
+    const __m256 mag = _mm256_permutevar8x32_ps(_mm256_loadu_ps(kE2M1), code);  // low 3 bits index
+    const __m256 sgn = _mm256_castsi256_ps(_mm256_slli_epi32(_mm256_srli_epi32(code, 3), 31));
+    return _mm256_mul_ps(_mm256_xor_ps(mag, sgn), scale);
+}
+
+// Same sums with AVX2: two 8-wide accumulators per row = 16 partial sums.
+template <int WF>
+__attribute__((target("avx2,fma"))) void dots_avx2(const void *w, const uint8_t *sc, const float *const *xs,
+                                                   int nr, int n, float *out)
+{
+    constexpr int STEP = WF == HF_MX ? 32 : 16;
     for (int r0 = 0; r0 < nr; r0 += kRowsPerDot) {
         const int m = nr - r0 < kRowsPerDot ? nr - r0 : kRowsPerDot;
         __m256 acc[kRowsPerDot][2];
         for (int r = 0; r < kRowsPerDot; ++r)
             acc[r][0] = acc[r][1] = _mm256_setzero_ps();
-        for (int c = 0; c < n; c += 16) {
-            __m256 w0, w1;
-            if (WBF) {
+        for (int c = 0; c < n; c += STEP) {
+            __m256 wv[4];
+            if (WF == HF_MX) {
+                const __m128i bytes = _mm_loadu_si128((const __m128i *)((const uint8_t *)w + c / 2));
+                const __m128i lo = _mm_and_si128(bytes, _mm_set1_epi8(0x0f));
+                const __m128i hi = _mm_and_si128(_mm_srli_epi16(bytes, 4), _mm_set1_epi8(0x0f));
+                const __m128i e0 = _mm_unpacklo_epi8(lo, hi), e1 = _mm_unpackhi_epi8(lo, hi);
+                const __m256 scale = _mm256_set1_ps(e8m0(sc[c / 32]));
+                wv[0] = e2m1x8(_mm256_cvtepu8_epi32(e0), scale);
+                wv[1] = e2m1x8(_mm256_cvtepu8_epi32(_mm_srli_si128(e0, 8)), scale);
+                wv[2] = e2m1x8(_mm256_cvtepu8_epi32(e1), scale);
+                wv[3] = e2m1x8(_mm256_cvtepu8_epi32(_mm_srli_si128(e1, 8)), scale);
+            } else if (WF == HF_BF16) {
                 const uint16_t *p = (const uint16_t *)w + c;
                 const __m128i a = _mm_loadu_si128((const __m128i *)p);
                 const __m128i b = _mm_loadu_si128((const __m128i *)(p + 8));
-                w0 = _mm256_castsi256_ps(_mm256_slli_epi32(_mm256_cvtepu16_epi32(a), 16));
-                w1 = _mm256_castsi256_ps(_mm256_slli_epi32(_mm256_cvtepu16_epi32(b), 16));
+                wv[0] = _mm256_castsi256_ps(_mm256_slli_epi32(_mm256_cvtepu16_epi32(a), 16));
+                wv[1] = _mm256_castsi256_ps(_mm256_slli_epi32(_mm256_cvtepu16_epi32(b), 16));
             } else {
-                w0 = _mm256_loadu_ps((const float *)w + c);
-                w1 = _mm256_loadu_ps((const float *)w + c + 8);
+                wv[0] = _mm256_loadu_ps((const float *)w + c);
+                wv[1] = _mm256_loadu_ps((const float *)w + c + 8);
             }
             for (int r = 0; r < m; ++r) {
-                acc[r][0] = _mm256_fmadd_ps(w0, _mm256_loadu_ps(xs[r0 + r] + c), acc[r][0]);
-                acc[r][1] = _mm256_fmadd_ps(w1, _mm256_loadu_ps(xs[r0 + r] + c + 8), acc[r][1]);
+                const float *xp = xs[r0 + r] + c;
+                for (int v = 0; v < STEP / 8; ++v)
+                    acc[r][v & 1] = _mm256_fmadd_ps(wv[v], _mm256_loadu_ps(xp + 8 * v), acc[r][v & 1]);
             }
         }
         for (int r = 0; r < m; ++r)
@@ -163,13 +206,37 @@ bool have_avx2()
     return v;
 }
 
-template <bool WBF>
-void dots(const void *w, const float *const *xs, int nr, int n, float *out)
+template <int WF>
+void dots(const void *w, const uint8_t *sc, const float *const *xs, int nr, int n, float *out)
 {
     if (have_avx2())
-        dots_avx2<WBF>(w, xs, nr, n, out);
+        dots_avx2<WF>(w, sc, xs, nr, n, out);
     else
-        dots_scalar<WBF>(w, xs, nr, n, out);
+        dots_scalar<WF>(w, sc, xs, nr, n, out);
+}
+
+// Row i of a weight section (element count n per row) and its scale row.
+struct RowRef {
+    const char *w;
+    const uint8_t *sc;
+};
+
+inline RowRef row_of(const void *blob, size_t off_w, size_t off_s, int wf, int i, int n)
+{
+    const char *b = (const char *)blob;
+    if (wf == HF_MX)
+        return {b + off_w + (size_t)i * n / 2, (const uint8_t *)b + off_s + (size_t)i * (n / 32)};
+    return {b + off_w + (size_t)i * n * (wf == HF_BF16 ? 2 : 4), nullptr};
+}
+
+void dots_any(int wf, RowRef row, const float *const *xs, int nr, int n, float *out)
+{
+    if (wf == HF_MX)
+        dots<HF_MX>(row.w, row.sc, xs, nr, n, out);
+    else if (wf == HF_BF16)
+        dots<HF_BF16>(row.w, row.sc, xs, nr, n, out);
+    else
+        dots<HF_F32>(row.w, row.sc, xs, nr, n, out);
 }
 
 }  // namespace
@@ -179,11 +246,8 @@ int host_experts(HostPool &pool, const ecf_shape &s, const BlobLayout &lay,
 {
     if (jobs.empty())
         return ECF_OK;
-    if (s.w_dtype == ECF_MXFP4)
-        return set_error(ECF_EUNSUPPORTED, "host experts: MXFP4 weights are not evaluated on the host");
     const int d = s.hidden, I = s.inter, k = s.top_k;
-    const bool wbf = s.w_dtype == ECF_BF16;
-    const size_t esz = wbf ? 2 : 4;
+    const int wf = s.w_dtype == ECF_MXFP4 ? HF_MX : s.w_dtype == ECF_BF16 ? HF_BF16 : HF_F32;
     // activations of every token in fp32
     std::vector<float> xf((size_t)T * d);
     if (s.a_dtype == ECF_BF16)
@@ -208,17 +272,11 @@ int host_experts(HostPool &pool, const ecf_shape &s, const BlobLayout &lay,
         for (int r = 0; r < nr; ++r)
             xs[r] = xf.data() + (size_t)(jb.rows[r] / k) * d;
         std::vector<float> a(nr), b(nr);
-        const char *wg = (const char *)jb.blob + lay.off[0], *wu = (const char *)jb.blob + lay.off[1];
         float *hj = h.data() + hoff[task / gu_chunks];
         const int i0 = (task % gu_chunks) * CH, i1 = std::min(I, i0 + CH);
         for (int i = i0; i < i1; ++i) {
-            if (wbf) {
-                dots<true>(wg + (size_t)i * d * esz, xs.data(), nr, d, a.data());
-                dots<true>(wu + (size_t)i * d * esz, xs.data(), nr, d, b.data());
-            } else {
-                dots<false>(wg + (size_t)i * d * esz, xs.data(), nr, d, a.data());
-                dots<false>(wu + (size_t)i * d * esz, xs.data(), nr, d, b.data());
-            }
+            dots_any(wf, row_of(jb.blob, lay.off[0], lay.off[3], wf, i, d), xs.data(), nr, d, a.data());
+            dots_any(wf, row_of(jb.blob, lay.off[1], lay.off[4], wf, i, d), xs.data(), nr, d, b.data());
             for (int r = 0; r < nr; ++r)
                 hj[(size_t)r * I + i] = a[r] / (1.0f + std::exp(-a[r])) * b[r];
         }
@@ -232,13 +290,9 @@ int host_experts(HostPool &pool, const ecf_shape &s, const BlobLayout &lay,
         for (int r = 0; r < nr; ++r)
             hs[r] = hj + (size_t)r * I;
         std::vector<float> o(nr);
-        const char *wd = (const char *)jb.blob + lay.off[2];
         const int o0 = (task % dn_chunks) * CH, o1 = std::min(d, o0 + CH);
         for (int oo = o0; oo < o1; ++oo) {
-            if (wbf)
-                dots<true>(wd + (size_t)oo * I * esz, hs.data(), nr, I, o.data());
-            else
-                dots<false>(wd + (size_t)oo * I * esz, hs.data(), nr, I, o.data());
+            dots_any(wf, row_of(jb.blob, lay.off[2], lay.off[5], wf, oo, I), hs.data(), nr, I, o.data());
             for (int r = 0; r < nr; ++r)
                 y[(size_t)jb.rows[r] * d + oo] = o[r];
         }

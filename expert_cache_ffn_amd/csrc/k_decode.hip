@@ -18,78 +18,155 @@
 
 namespace ecf {
 
-// Dot products of one weight row segment [kbeg, kend) against nt staged rows.
-// V weights per 16-byte load; group of 8 lanes covers 8*V elements per step.
-template <bool WBF>
-__device__ __forceinline__ void row_dots(const void *__restrict__ wrow, const float *__restrict__ xs,
-                                         int ld, int kbeg, int kend, int sub, int nt,
-                                         float acc[kDecodeNT])
+// Weight formats of the GEMV path.
+enum { WF_F32 = 0, WF_BF16 = 1, WF_MX = 2 };
+
+// Staged activation rows in LDS are padded by 4 floats after every 32, so the
+// 8 lanes of a group, which read 16-byte pieces 32 (MXFP4), 8 (bf16) or 4 (fp32)
+// floats apart, hit distinct banks.  A 16-byte piece never crosses a pad.
+__device__ __forceinline__ int xpad(int c) { return c + ((c >> 5) << 2); }
+__host__ __device__ constexpr int xpad_len(int n) { return n + (n >> 3); }
+
+// Stage one activation row of n elements (a multiple of 8; src 16-byte aligned)
+// as padded fp32 in LDS, 16 bytes per thread and load.
+template <bool SRC_BF16>
+__device__ __forceinline__ void stage_row(float *__restrict__ dst, const void *__restrict__ src, int n, int tid)
 {
-    constexpr int V = WBF ? 8 : 4;
-    constexpr int UNR = 4;
-    for (int c0 = kbeg + sub * V; c0 < kend; c0 += 8 * V * UNR) {
-        uint4 wv[UNR];
-#pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-            const int c = c0 + u * 8 * V;
-            if (c < kend)
-                wv[u] = ld_nt16((const char *)wrow + (size_t)c * (WBF ? 2 : 4));
+    if (SRC_BF16) {
+        for (int c = tid * 8; c < n; c += 2048) {
+            const uint4 v = *reinterpret_cast<const uint4 *>((const uint16_t *)src + c);
+            *reinterpret_cast<float4 *>(dst + xpad(c)) = make_float4(bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y));
+            *reinterpret_cast<float4 *>(dst + xpad(c + 4)) =
+                make_float4(bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w));
         }
+    } else {
+        for (int c = tid * 4; c < n; c += 1024)
+            *reinterpret_cast<float4 *>(dst + xpad(c)) = *reinterpret_cast<const float4 *>((const float *)src + c);
+    }
+}
+
+// part[q][i % 4] += w[i] * xs[q][c + i] over the nt staged rows.
+template <int N>
+__device__ __forceinline__ void fma_rows(const float (&w)[N], const float *__restrict__ xs, int ld, int c, int nt,
+                                         float (&part)[kDecodeNT][4])
+{
 #pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-            const int c = c0 + u * 8 * V;
-            if (c >= kend)
-                break;
-            float wf[V];
-            if (WBF) {
-                const uint32_t p[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
+    for (int q = 0; q < kDecodeNT; ++q) {
+        if (q < nt) {
+            const float *xp = xs + q * xpad_len(ld);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    wf[2 * i] = bf_lo(p[i]);
-                    wf[2 * i + 1] = bf_hi(p[i]);
-                }
-            } else {
-                wf[0] = __uint_as_float(wv[u].x);
-                wf[1] = __uint_as_float(wv[u].y);
-                wf[2] = __uint_as_float(wv[u].z);
-                wf[3] = __uint_as_float(wv[u].w);
-            }
-#pragma unroll
-            for (int q = 0; q < kDecodeNT; ++q) {
-                if (q < nt) {
-                    const float *xp = xs + q * ld + c;
-                    float s = acc[q];
-#pragma unroll
-                    for (int i = 0; i < V; i += 4) {
-                        const float4 xv = *reinterpret_cast<const float4 *>(xp + i);
-                        s = fmaf(wf[i], xv.x, s);
-                        s = fmaf(wf[i + 1], xv.y, s);
-                        s = fmaf(wf[i + 2], xv.z, s);
-                        s = fmaf(wf[i + 3], xv.w, s);
-                    }
-                    acc[q] = s;
-                }
+            for (int i = 0; i < N; i += 4) {
+                const float4 xv = *reinterpret_cast<const float4 *>(xp + xpad(c + i));
+                part[q][0] = fmaf(w[i], xv.x, part[q][0]);
+                part[q][1] = fmaf(w[i + 1], xv.y, part[q][1]);
+                part[q][2] = fmaf(w[i + 2], xv.z, part[q][2]);
+                part[q][3] = fmaf(w[i + 3], xv.w, part[q][3]);
             }
         }
     }
 }
 
-__device__ __forceinline__ float load_act(const void *x, bool abf, size_t i)
+// One lane's share of a weight row segment [kbeg, kend), held in registers: a
+// 16-byte load holds V weights (f32 4, bf16 8, MXFP4 32 = one E8M0 scale
+// group, whose scale byte srow[c / 32] is loaded beside it); a group of 8
+// lanes covers 8*V elements per load and UNR loads.  MXFP4 elements are
+// expanded to fp32 by v_cvt_scalef32_pk_f32_fp4 (element 2i in the low nibble
+// of byte i; the power-of-two scale is applied exactly).
+template <int WF>
+struct RowRegs {
+    static constexpr int V = WF == WF_MX ? 32 : WF == WF_BF16 ? 8 : 4;
+    // a 16-byte MXFP4 load feeds 4x the arithmetic of a bf16 one, so it takes
+    // twice the loads in flight
+    static constexpr int UNR = WF == WF_MX ? 8 : 4;
+    static constexpr int SPAN = 8 * V * UNR;  // elements one group covers per batch
+    uint4 wv[UNR];
+    uint32_t sb[UNR];
+
+    __device__ __forceinline__ void load(const void *__restrict__ wrow, const uint8_t *__restrict__ srow, int c0,
+                                         int kend)
+    {
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int c = c0 + u * 8 * V;
+            if (c < kend) {
+                const size_t byte = WF == WF_MX ? (size_t)c / 2 : (size_t)c * (WF == WF_BF16 ? 2 : 4);
+                wv[u] = ld_nt16((const char *)wrow + byte);
+                if (WF == WF_MX)
+                    sb[u] = srow[c / 32];
+            }
+        }
+    }
+
+    __device__ __forceinline__ void apply(const float *__restrict__ xs, int ld, int c0, int kend, int nt,
+                                          float (&part)[kDecodeNT][4]) const
+    {
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int c = c0 + u * 8 * V;
+            if (c >= kend)
+                break;
+            const uint32_t p[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
+            if (WF == WF_MX) {
+                const float sc = __uint_as_float(sb[u] == 0 ? 0x00400000u : (sb[u] << 23));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {  // 8 elements per dword
+                    const f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p[i], sc, 0);
+                    const f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p[i], sc, 1);
+                    const f32x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p[i], sc, 2);
+                    const f32x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p[i], sc, 3);
+                    const float wf[8] = {v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+                    fma_rows(wf, xs, ld, c + 8 * i, nt, part);
+                }
+            } else if (WF == WF_BF16) {
+                float wf[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    wf[2 * i] = bf_lo(p[i]);
+                    wf[2 * i + 1] = bf_hi(p[i]);
+                }
+                fma_rows(wf, xs, ld, c, nt, part);
+            } else {
+                float wf[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    wf[i] = __uint_as_float(p[i]);
+                fma_rows(wf, xs, ld, c, nt, part);
+            }
+        }
+    }
+};
+
+// Dot products of one weight row segment [kbeg, kend) against nt staged rows;
+// the segment streams through registers one batch of UNR loads at a time.
+// Each row keeps 4 independent partial sums (element i of every 4 goes to
+// sum i), so the FMA chains are a quarter as long.
+template <int WF>
+__device__ __forceinline__ void row_dots(const void *__restrict__ wrow, const uint8_t *__restrict__ srow,
+                                         const float *__restrict__ xs, int ld, int kbeg, int kend, int sub, int nt,
+                                         float acc[kDecodeNT])
 {
-    return abf ? bf_to_f(((const uint16_t *)x)[i]) : ((const float *)x)[i];
+    RowRegs<WF> rr;
+    float part[kDecodeNT][4] = {};
+    for (int c = kbeg + sub * RowRegs<WF>::V; c < kend; c += RowRegs<WF>::SPAN) {
+        rr.load(wrow, srow, c, kend);
+        rr.apply(xs, ld, c, kend, nt, part);
+    }
+#pragma unroll
+    for (int q = 0; q < kDecodeNT; ++q)
+        acc[q] += (part[q][0] + part[q][1]) + (part[q][2] + part[q][3]);
 }
 
 // gate/up + SwiGLU.  Block = IB intermediate rows (gate and up) of one active
 // expert, split into KP parts along d.  grid = (I / IB, max active experts).
-template <bool WBF, bool ABF, int IB, int KP>
+template <int WF, bool ABF, int IB, int KP>
 __global__ __launch_bounds__(256) void k_decode_gateup(
-    const uint64_t *__restrict__ ptrs, size_t off_gate, size_t off_up,
+    const uint64_t *__restrict__ ptrs, size_t off_gate, size_t off_up, size_t off_sgate, size_t off_sup,
     const int32_t *__restrict__ active, const int32_t *__restrict__ n_active,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm,
     const void *__restrict__ x, int d, int I, int k, int E, int R, int ntp, float *__restrict__ H)
 {
     static_assert(2 * IB * KP == 32, "32 groups of 8 lanes per block");
-    extern __shared__ float xs[];  // [min(kDecodeNT, T)][d]; an expert has at most T rows
+    extern __shared__ float xs[];  // [min(kDecodeNT, T)][xpad_len(d)]; an expert has at most T rows
     __shared__ float red[KP][2 * IB][kDecodeNT];
     if ((int)blockIdx.y >= *n_active)
         return;
@@ -100,59 +177,64 @@ __global__ __launch_bounds__(256) void k_decode_gateup(
     const int r0 = offsets[e], ne = offsets[e + 1] - r0;
     if (!blob || r0 < 0 || ne <= 0 || r0 + ne > R)
         return;
-    const int i0 = blockIdx.x * IB;
     const int tid = threadIdx.x, lane = tid & 63, sub = lane & 7;
     const int g = tid >> 3;  // group 0..31
     const int rho = g % (2 * IB), kap = g / (2 * IB);
     const size_t sec = rho < IB ? off_gate : off_up;
+    const size_t ssec = rho < IB ? off_sgate : off_sup;
+    const int i0 = blockIdx.x * IB;
     const int irow = i0 + (rho % IB);
-    const char *wrow = (const char *)blob + sec + (size_t)irow * d * (WBF ? 2 : 4);
+    const char *wrow = (const char *)blob + sec +
+                       (WF == WF_MX ? (size_t)irow * d / 2 : (size_t)irow * d * (WF == WF_BF16 ? 2 : 4));
+    const uint8_t *srow = (const uint8_t *)blob + ssec + (size_t)irow * (d / 32);
     const int Lk = d / KP, kbeg = kap * Lk, kend = kbeg + Lk;
     for (int tp = 0; tp < ne; tp += ntp) {
         const int nt = min(ntp, ne - tp);
         for (int q = 0; q < nt; ++q) {
             const size_t t = (size_t)(perm[r0 + tp + q] / k);
-            for (int c = tid; c < d; c += 256)
-                xs[q * d + c] = load_act(x, ABF, t * d + c);
+            stage_row<ABF>(xs + q * xpad_len(d), ABF ? (const void *)((const uint16_t *)x + t * d)
+                                                     : (const void *)((const float *)x + t * d), d, tid);
         }
         __syncthreads();
-        float acc[kDecodeNT] = {};
-        row_dots<WBF>(wrow, xs, d, kbeg, kend, sub, nt, acc);
+        {
+            float acc[kDecodeNT] = {};
+            row_dots<WF>(wrow, srow, xs, d, kbeg, kend, sub, nt, acc);
 #pragma unroll
-        for (int q = 0; q < kDecodeNT; ++q) {
-            acc[q] += __shfl_xor(acc[q], 1, 64);
-            acc[q] += __shfl_xor(acc[q], 2, 64);
-            acc[q] += __shfl_xor(acc[q], 4, 64);
-        }
-        if (sub == 0)
-#pragma unroll
-            for (int q = 0; q < kDecodeNT; ++q)
-                red[kap][rho][q] = acc[q];
-        __syncthreads();
-        if (tid < IB * nt) {
-            const int il = tid % IB, q = tid / IB;
-            float a = 0.f, b = 0.f;
-#pragma unroll
-            for (int p = 0; p < KP; ++p) {
-                a += red[p][il][q];
-                b += red[p][IB + il][q];
+            for (int q = 0; q < kDecodeNT; ++q) {
+                acc[q] += __shfl_xor(acc[q], 1, 64);
+                acc[q] += __shfl_xor(acc[q], 2, 64);
+                acc[q] += __shfl_xor(acc[q], 4, 64);
             }
-            H[(size_t)(r0 + tp + q) * I + i0 + il] = silu_mul(a, b);
+            if (sub == 0)
+#pragma unroll
+                for (int q = 0; q < kDecodeNT; ++q)
+                    red[kap][rho][q] = acc[q];
+            __syncthreads();
+            if (tid < IB * nt) {
+                const int il = tid % IB, q = tid / IB;
+                float a = 0.f, b = 0.f;
+#pragma unroll
+                for (int p = 0; p < KP; ++p) {
+                    a += red[p][il][q];
+                    b += red[p][IB + il][q];
+                }
+                H[(size_t)(r0 + tp + q) * I + i0 + il] = silu_mul(a, b);
+            }
+            __syncthreads();
         }
-        __syncthreads();
     }
 }
 
 // down projection: Y[r][o] = W_down[e][o] . h[r].  Block = OB output rows of
 // one active expert, KP parts along I.  grid = (d / OB, max active experts).
-template <bool WBF, int OB, int KP>
+template <int WF, int OB, int KP>
 __global__ __launch_bounds__(256) void k_decode_down(
-    const uint64_t *__restrict__ ptrs, size_t off_down, const int32_t *__restrict__ active,
+    const uint64_t *__restrict__ ptrs, size_t off_down, size_t off_sdown, const int32_t *__restrict__ active,
     const int32_t *__restrict__ n_active, const int32_t *__restrict__ offsets,
     const float *__restrict__ H, int d, int I, int E, int R, int ntp, float *__restrict__ Y)
 {
     static_assert(OB * KP == 32, "32 groups of 8 lanes per block");
-    extern __shared__ float hs[];  // [min(kDecodeNT, T)][I]
+    extern __shared__ float hs[];  // [min(kDecodeNT, T)][xpad_len(I)]
     __shared__ float red[KP][OB][kDecodeNT];
     if ((int)blockIdx.y >= *n_active)
         return;
@@ -163,40 +245,46 @@ __global__ __launch_bounds__(256) void k_decode_down(
     const int r0 = offsets[e], ne = offsets[e + 1] - r0;
     if (!blob || r0 < 0 || ne <= 0 || r0 + ne > R)
         return;
-    const int o0 = blockIdx.x * OB;
     const int tid = threadIdx.x, lane = tid & 63, sub = lane & 7;
     const int g = tid >> 3;
     const int rho = g % OB, kap = g / OB;
-    const char *wrow = (const char *)blob + off_down + (size_t)(o0 + rho) * I * (WBF ? 2 : 4);
+    const int o0 = blockIdx.x * OB;
+    const size_t orow = (size_t)(o0 + rho);
+    const char *wrow = (const char *)blob + off_down +
+                       (WF == WF_MX ? orow * I / 2 : orow * I * (WF == WF_BF16 ? 2 : 4));
+    const uint8_t *srow = (const uint8_t *)blob + off_sdown + orow * (I / 32);
     const int Lk = I / KP, kbeg = kap * Lk, kend = kbeg + Lk;
     for (int tp = 0; tp < ne; tp += ntp) {
         const int nt = min(ntp, ne - tp);
         for (int q = 0; q < nt; ++q)
-            for (int c = tid; c < I; c += 256)
-                hs[q * I + c] = H[(size_t)(r0 + tp + q) * I + c];
+            for (int c = tid * 4; c < I; c += 1024)  // I is a multiple of 64: whole float4s
+                *reinterpret_cast<float4 *>(hs + q * xpad_len(I) + xpad(c)) =
+                    *reinterpret_cast<const float4 *>(H + (size_t)(r0 + tp + q) * I + c);
         __syncthreads();
-        float acc[kDecodeNT] = {};
-        row_dots<WBF>(wrow, hs, I, kbeg, kend, sub, nt, acc);
+        {
+            float acc[kDecodeNT] = {};
+            row_dots<WF>(wrow, srow, hs, I, kbeg, kend, sub, nt, acc);
 #pragma unroll
-        for (int q = 0; q < kDecodeNT; ++q) {
-            acc[q] += __shfl_xor(acc[q], 1, 64);
-            acc[q] += __shfl_xor(acc[q], 2, 64);
-            acc[q] += __shfl_xor(acc[q], 4, 64);
+            for (int q = 0; q < kDecodeNT; ++q) {
+                acc[q] += __shfl_xor(acc[q], 1, 64);
+                acc[q] += __shfl_xor(acc[q], 2, 64);
+                acc[q] += __shfl_xor(acc[q], 4, 64);
+            }
+            if (sub == 0)
+#pragma unroll
+                for (int q = 0; q < kDecodeNT; ++q)
+                    red[kap][rho][q] = acc[q];
+            __syncthreads();
+            if (tid < OB * nt) {
+                const int ol = tid % OB, q = tid / OB;
+                float sum = 0.f;
+#pragma unroll
+                for (int p = 0; p < KP; ++p)
+                    sum += red[p][ol][q];
+                Y[(size_t)(r0 + tp + q) * d + o0 + ol] = sum;
+            }
+            __syncthreads();
         }
-        if (sub == 0)
-#pragma unroll
-            for (int q = 0; q < kDecodeNT; ++q)
-                red[kap][rho][q] = acc[q];
-        __syncthreads();
-        if (tid < OB * nt) {
-            const int ol = tid % OB, q = tid / OB;
-            float s = 0.f;
-#pragma unroll
-            for (int p = 0; p < KP; ++p)
-                s += red[p][ol][q];
-            Y[(size_t)(r0 + tp + q) * d + o0 + ol] = s;
-        }
-        __syncthreads();
     }
 }
 
@@ -260,21 +348,22 @@ int launch_decode_gateup(const ecf_shape &s, const ExpertTables &ex, const Route
     constexpr int IB = 8, KP = 2;
     dim3 grid(s.inter / IB, maxa);
     const int ntp = std::min(kDecodeNT, T);  // an expert has at most T rows
-    const size_t sh = sizeof(float) * ntp * s.hidden;
+    const size_t sh = sizeof(float) * ntp * xpad_len(s.hidden);
     ProfScope p("decode_gateup", st);
-    const bool wbf = s.w_dtype == ECF_BF16, abf = s.a_dtype == ECF_BF16;
-#define ECF_GU(WB, AB)                                                                              \
-    hipLaunchKernelGGL((k_decode_gateup<WB, AB, IB, KP>), grid, dim3(256), sh, st, ex.ptrs,          \
-                       ex.lay.off[0], ex.lay.off[1], o.active, o.n_active, o.offsets, o.perm, x,      \
-                       s.hidden, s.inter, s.top_k, s.n_experts, R, ntp, H)
-    if (wbf && abf)
-        ECF_GU(true, true);
-    else if (wbf)
-        ECF_GU(true, false);
+    const bool abf = s.a_dtype == ECF_BF16;
+#define ECF_GU(WFV, AB)                                                                             \
+    hipLaunchKernelGGL((k_decode_gateup<WFV, AB, IB, KP>), grid, dim3(256), sh, st, ex.ptrs,         \
+                       ex.lay.off[0], ex.lay.off[1], ex.lay.off[3], ex.lay.off[4], o.active,          \
+                       o.n_active, o.offsets, o.perm, x, s.hidden, s.inter, s.top_k, s.n_experts, R,  \
+                       ntp, H)
+    if (s.w_dtype == ECF_MXFP4)  // bf16 activations (checked with the shape)
+        ECF_GU(WF_MX, true);
+    else if (s.w_dtype == ECF_BF16)
+        ECF_GU(WF_BF16, true);
     else if (abf)
-        ECF_GU(false, true);
+        ECF_GU(WF_F32, true);
     else
-        ECF_GU(false, false);
+        ECF_GU(WF_F32, false);
 #undef ECF_GU
     ECF_HIP_CHECK(hipGetLastError());
     return ECF_OK;
@@ -288,15 +377,19 @@ int launch_decode_down(const ecf_shape &s, const ExpertTables &ex, const RouteOu
     constexpr int OB = 32, KP = 1;
     dim3 grid(s.hidden / OB, maxa);
     const int ntp = std::min(kDecodeNT, T);
-    const size_t sh = sizeof(float) * ntp * s.inter;
+    const size_t sh = sizeof(float) * ntp * xpad_len(s.inter);
     ProfScope p("decode_down", st);
-    if (s.w_dtype == ECF_BF16)
-        hipLaunchKernelGGL((k_decode_down<true, OB, KP>), grid, dim3(256), sh, st, ex.ptrs, ex.lay.off[2],
-                           o.active, o.n_active, o.offsets, H, s.hidden, s.inter, s.n_experts, R, ntp, Y);
+#define ECF_DN(WFV)                                                                                 \
+    hipLaunchKernelGGL((k_decode_down<WFV, OB, KP>), grid, dim3(256), sh, st, ex.ptrs, ex.lay.off[2],  \
+                       ex.lay.off[5], o.active, o.n_active, o.offsets, H, s.hidden, s.inter,          \
+                       s.n_experts, R, ntp, Y)
+    if (s.w_dtype == ECF_MXFP4)
+        ECF_DN(WF_MX);
+    else if (s.w_dtype == ECF_BF16)
+        ECF_DN(WF_BF16);
     else
-        hipLaunchKernelGGL((k_decode_down<false, OB, KP>), grid, dim3(256), sh, st, ex.ptrs,
-                           ex.lay.off[2], o.active, o.n_active, o.offsets, H, s.hidden, s.inter, s.n_experts,
-                           R, ntp, Y);
+        ECF_DN(WF_F32);
+#undef ECF_DN
     ECF_HIP_CHECK(hipGetLastError());
     return ECF_OK;
 }

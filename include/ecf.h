@@ -63,7 +63,7 @@ typedef enum { ECF_F32 = 0, ECF_BF16 = 1, ECF_MXFP4 = 2 } ecf_dtype;
 typedef struct {
     int32_t hidden;      /* d: model width; multiple of 256 */
     int32_t inter;       /* I: expert intermediate width; multiple of 64 (of 128 for
-                            the prefill path, which MXFP4 weights always take) */
+                            the prefill path) */
     int32_t n_experts;   /* E: routed experts per layer, 1..1024 */
     int32_t top_k;       /* k: experts per token, 1..min(E, 32) */
     int32_t w_dtype;     /* expert weight encoding, ecf_dtype */
@@ -202,7 +202,9 @@ typedef struct {
     double b_p, b_h;             /* bandwidth figures for qstar_split (any unit, same for both) */
     int32_t q_mode;              /* ECF_Q_*: AUTO uses qstar_split; the others are for tests */
     int32_t q_fixed;             /* q for ECF_Q_FIXED (clamped to [0, m]) */
-    int32_t path;                /* ECF_PATH_*: AUTO picks by rows per expert and dtype */
+    int32_t path;                /* ECF_PATH_*: AUTO takes the decode GEMVs for fp32 weights
+                                    and, for bf16 / MXFP4, while T <= 64 or I % 128 != 0;
+                                    the prefill grouped GEMM otherwise (bf16 / MXFP4 only) */
     /* buffers */
     void *d_ws;                  /* workspace, >= ecf_workspace_bytes(shape, T) bytes, 256-B aligned */
     size_t ws_bytes;
@@ -221,7 +223,7 @@ typedef struct {
 /*
  * out[t][:] = residual[t][:] + sum_{j=0..k-1} gate[t][j] * FFN_{idx[t][j]}(x[t])
  * with FFN_e(v) = W_down[e] . (silu(W_gate[e] . v) * (W_up[e] . v)), x [T][d]
- * in a_dtype, out [T][d] fp32.  All-resident mode is fully asynchronous on
+ * in a_dtype (16-byte aligned, else ECF_EINVAL), out [T][d] fp32.  All-resident mode is fully asynchronous on
  * args->stream.  Cache mode blocks the calling thread once on the routing
  * readback (the q* decision is taken on the host from the step's miss count
  * [TF "Bandwidth-adaptive execution (q* policy)"]), computes host-assigned
@@ -236,8 +238,8 @@ int moe_layer_forward(const ecf_layer_args *args, const void *d_x, int32_t n_tok
  * f listed per expert, evaluated by n_threads host threads (0 = default) the
  * same way a forward call evaluates host-assigned experts [TF "Bandwidth-
  * adaptive execution (q* policy)": missed experts not copied run on the CPU
- * straight from host memory].  h_blobs[i] is the host blob of job i (bf16 or
- * fp32 weights), rows of job i are rows[sum(n_rows[<i]) .. + n_rows[i]];
+ * straight from host memory].  h_blobs[i] is the host blob of job i (fp32, bf16
+ * or MXFP4 weights), rows of job i are rows[sum(n_rows[<i]) .. + n_rows[i]];
  * h_x [T][d] in a_dtype, h_y [T*k][d] fp32 (only listed rows written).  No
  * GPU is touched.
  */
@@ -258,7 +260,7 @@ int ecf_host_experts(const ecf_shape *shape, int32_t n_jobs, const void *const *
  *   b_h         b_p_conc + b_cpu_conc: the host bandwidth the two share.
  * All in GB/s (1e9 B/s).  Pass (b_p_conc, b_h) as (b_p, b_h) to qstar_split or
  * ecf_layer_args.  h_blobs: n_blobs pinned host expert blobs of `shape` (fp32 or
- * bf16 weights; MXFP4 -> ECF_EUNSUPPORTED), read only.  d_buf: device scratch of
+ * bf16 or MXFP4 weights), read only.  d_buf: device scratch of
  * d_buf_bytes >= one blob (ECF_ENOSPC otherwise), overwritten.  host_threads 0 =
  * min(16, hardware threads).  Allocates its thread pool; blocks until done.
  * ECF_EINVAL for NULL pointers, n_blobs < 1 or seconds <= 0; ECF_EHIP on a HIP

@@ -52,10 +52,11 @@ def _run(layer_obj, a, x, T, d):
     return out.cpu().numpy(), st
 
 
+@pytest.mark.parametrize("w_dtype", ["bf16", "mxfp4"])
 @pytest.mark.parametrize("mode,q_fixed", [(ecf.ECF_Q_ALL_GPU, 0), (ecf.ECF_Q_ALL_HOST, 0), (ecf.ECF_Q_FIXED, 2),
                                           (ecf.ECF_Q_AUTO, 0)])
-def test_split_invariance_small(mode, q_fixed):
-    cfg = syn.gen.Config(100, "cs", (4,), 512, 16, 256, 4, "bf16", "bf16", "zipf", layers=3)
+def test_split_invariance_small(mode, q_fixed, w_dtype):
+    cfg = syn.gen.Config(100, "cs", (4,), 512, 16, 256, 4, w_dtype, "bf16", "zipf", layers=3)
     L, T, d = 3, 4, cfg.hidden
     cs = CachedSetup(cfg, L, n_slots=10)
     lay = Layer(cs.shape, T)

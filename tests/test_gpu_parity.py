@@ -134,7 +134,7 @@ def test_prefill_mxfp4_small(T, E, k, I):
                     cid=80 + E)
     say(f"case: prefill mxfp4 T={T} E={E} k={k}")
     c = Case(cfg, T)
-    res = c.run()
+    res = c.run(path=ecf.ECF_PATH_PREFILL)
     assert res["stats"]["path"] == ecf.ECF_PATH_PREFILL
     compare(res, c.oracle(), TOL["mxfp4"], f"mxfp4 T={T} E={E}")
 
@@ -148,6 +148,49 @@ def test_prefill_mxfp4_full_size_sampled():
     compare(res, c.oracle(tokens=toks), TOL["mxfp4"], "mxfp4 full")
     del c
     torch.cuda.empty_cache()
+
+
+# ---- decode MXFP4 (GEMV over 4-bit weights, h fp32) ------------------------------------------
+
+# The GEMV expands each E2M1 element times its E8M0 scale exactly and keeps h in
+# fp32, so it meets a much tighter bound than the MXFP4 parity bar: the only
+# error left is fp32 summation order.
+MX_DECODE_TOL = 1e-4
+
+
+@pytest.mark.parametrize("T,E,k,I", [(1, 8, 2, 192), (5, 8, 8, 256), (16, 16, 4, 128), (37, 8, 2, 64)])
+def test_decode_mxfp4_small(T, E, k, I):
+    cfg = cfg_small(experts=E, top_k=k, inter=I, w_dtype="mxfp4", cid=110 + E + I // 64)
+    say(f"case: decode mxfp4 T={T} E={E} k={k} I={I}")
+    c = Case(cfg, T)
+    res = c.run()
+    assert res["stats"]["path"] == ecf.ECF_PATH_DECODE
+    compare(res, c.oracle(), MX_DECODE_TOL, f"decode mxfp4 T={T} E={E}")
+    assert MX_DECODE_TOL <= TOL["mxfp4"]
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_decode_mxfp4_full_size(T):
+    """The decode layer shape (d 4096, 256 experts, I 1024, top-6) with MXFP4 experts."""
+    import dataclasses
+    cfg = dataclasses.replace(syn.CONFIGS["decode"], w_dtype="mxfp4", cid=120)
+    say(f"case: decode mxfp4 full size T={T}")
+    c = Case(cfg, T, gen_device="cuda")
+    res = c.run()
+    assert res["stats"]["path"] == ecf.ECF_PATH_DECODE
+    compare(res, c.oracle(), MX_DECODE_TOL, f"decode mxfp4 full T={T}")
+    del c
+    torch.cuda.empty_cache()
+
+
+def test_mxfp4_decode_and_prefill_paths_agree():
+    cfg = cfg_small(experts=16, top_k=4, inter=256, w_dtype="mxfp4", cid=125)
+    c = Case(cfg, 40)
+    a = c.run(path=ecf.ECF_PATH_DECODE)
+    b = c.run(path=ecf.ECF_PATH_PREFILL)
+    rms = np.sqrt(np.mean(a["out"] ** 2))
+    assert np.max(np.abs(a["out"] - b["out"])) <= TOL["mxfp4"] * rms
+    assert np.array_equal(a["perm"], b["perm"])
 
 
 # ---- properties ----------------------------------------------------------------------------
