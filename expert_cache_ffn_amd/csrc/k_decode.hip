@@ -45,6 +45,43 @@ __device__ __forceinline__ void stage_row(float *__restrict__ dst, const void *_
     }
 }
 
+// bf16 activation rows staged as bf16 (exact copies) for the dot2 path: padded
+// by 8 elements (16 bytes) after every 32, so the 16-byte pieces the 8 lanes
+// of a group read (64 bytes apart for MXFP4, 16 for bf16 weights) hit
+// distinct banks.
+__device__ __forceinline__ int xpadh(int c) { return c + ((c >> 5) << 3); }
+__host__ __device__ constexpr int xpadh_len(int n) { return n + (n >> 2); }
+
+__device__ __forceinline__ void stage_row_bf16(uint16_t *__restrict__ dst, const uint16_t *__restrict__ src, int n,
+                                               int tid)
+{
+    for (int c = tid * 8; c < n; c += 2048)
+        *reinterpret_cast<uint4 *>(dst + xpadh(c)) = *reinterpret_cast<const uint4 *>(src + c);
+}
+
+// a.lo * b.lo + a.hi * b.hi + c over bf16 pairs (products exact), fp32 sum.
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                           false);
+}
+
+// part[q][i] += w-pair i . x-pair i for the 4 bf16 pairs at element c (c % 8 == 0).
+__device__ __forceinline__ void dot2_rows(const uint32_t (&w)[4], const uint16_t *__restrict__ xh, int ldp, int c,
+                                          int nt, float (&part)[kDecodeNT][4])
+{
+#pragma unroll
+    for (int q = 0; q < kDecodeNT; ++q) {
+        if (q < nt) {
+            const uint4 xv = *reinterpret_cast<const uint4 *>(xh + q * ldp + xpadh(c));
+            part[q][0] = dot2(w[0], xv.x, part[q][0]);
+            part[q][1] = dot2(w[1], xv.y, part[q][1]);
+            part[q][2] = dot2(w[2], xv.z, part[q][2]);
+            part[q][3] = dot2(w[3], xv.w, part[q][3]);
+        }
+    }
+}
+
 // part[q][i % 4] += w[i] * xs[q][c + i] over the nt staged rows.
 template <int N>
 __device__ __forceinline__ void fma_rows(const float (&w)[N], const float *__restrict__ xs, int ld, int c, int nt,
@@ -134,6 +171,34 @@ struct RowRegs {
             }
         }
     }
+
+    // Same sums against bf16-staged activations with bf16-pair dot products
+    // (bf16 or MXFP4 weights; MXFP4 expands to bf16 pairs, exactly).
+    __device__ __forceinline__ void apply2(const uint16_t *__restrict__ xh, int ldp, int c0, int kend, int nt,
+                                           float (&part)[kDecodeNT][4]) const
+    {
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int c = c0 + u * 8 * V;
+            if (c >= kend)
+                break;
+            const uint32_t p[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
+            if (WF == WF_MX) {
+                const float sc = __uint_as_float(sb[u] == 0 ? 0x00400000u : (sb[u] << 23));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {  // 8 elements per dword
+                    const uint32_t w[4] = {
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(p[i], sc, 0)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(p[i], sc, 1)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(p[i], sc, 2)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(p[i], sc, 3))};
+                    dot2_rows(w, xh, ldp, c + 8 * i, nt, part);
+                }
+            } else {
+                dot2_rows(p, xh, ldp, c, nt, part);
+            }
+        }
+    }
 };
 
 // Dot products of one weight row segment [kbeg, kend) against nt staged rows;
@@ -156,8 +221,28 @@ __device__ __forceinline__ void row_dots(const void *__restrict__ wrow, const ui
         acc[q] += (part[q][0] + part[q][1]) + (part[q][2] + part[q][3]);
 }
 
+// row_dots against bf16-staged activations (bf16 or MXFP4 weights).
+template <int WF>
+__device__ __forceinline__ void row_dots2(const void *__restrict__ wrow, const uint8_t *__restrict__ srow,
+                                          const uint16_t *__restrict__ xh, int ldp, int kbeg, int kend, int sub,
+                                          int nt, float acc[kDecodeNT])
+{
+    RowRegs<WF> rr;
+    float part[kDecodeNT][4] = {};
+    for (int c = kbeg + sub * RowRegs<WF>::V; c < kend; c += RowRegs<WF>::SPAN) {
+        rr.load(wrow, srow, c, kend);
+        rr.apply2(xh, ldp, c, kend, nt, part);
+    }
+#pragma unroll
+    for (int q = 0; q < kDecodeNT; ++q)
+        acc[q] += (part[q][0] + part[q][1]) + (part[q][2] + part[q][3]);
+}
+
 // gate/up + SwiGLU.  Block = IB intermediate rows (gate and up) of one active
 // expert, split into KP parts along d.  grid = (I / IB, max active experts).
+// bf16 activations with bf16 or MXFP4 weights stay bf16 in LDS and meet the
+// weights in bf16-pair dot products (half the LDS reads and FMA instructions of
+// the fp32 form; every product is exact either way).
 template <int WF, bool ABF, int IB, int KP>
 __global__ __launch_bounds__(256) void k_decode_gateup(
     const uint64_t *__restrict__ ptrs, size_t off_gate, size_t off_up, size_t off_sgate, size_t off_sup,
@@ -166,7 +251,10 @@ __global__ __launch_bounds__(256) void k_decode_gateup(
     const void *__restrict__ x, int d, int I, int k, int E, int R, int ntp, float *__restrict__ H)
 {
     static_assert(2 * IB * KP == 32, "32 groups of 8 lanes per block");
-    extern __shared__ float xs[];  // [min(kDecodeNT, T)][xpad_len(d)]; an expert has at most T rows
+    constexpr bool DOT2 = ABF && WF != WF_F32;
+    // [min(kDecodeNT, T)][xpadh_len(d)] bf16 (DOT2) or [..][xpad_len(d)] fp32; an expert has at most T rows
+    extern __shared__ float xs[];
+    uint16_t *xh = reinterpret_cast<uint16_t *>(xs);
     __shared__ float red[KP][2 * IB][kDecodeNT];
     if ((int)blockIdx.y >= *n_active)
         return;
@@ -192,13 +280,19 @@ __global__ __launch_bounds__(256) void k_decode_gateup(
         const int nt = min(ntp, ne - tp);
         for (int q = 0; q < nt; ++q) {
             const size_t t = (size_t)(perm[r0 + tp + q] / k);
-            stage_row<ABF>(xs + q * xpad_len(d), ABF ? (const void *)((const uint16_t *)x + t * d)
-                                                     : (const void *)((const float *)x + t * d), d, tid);
+            if (DOT2)
+                stage_row_bf16(xh + q * xpadh_len(d), (const uint16_t *)x + t * d, d, tid);
+            else
+                stage_row<ABF>(xs + q * xpad_len(d), ABF ? (const void *)((const uint16_t *)x + t * d)
+                                                         : (const void *)((const float *)x + t * d), d, tid);
         }
         __syncthreads();
         {
             float acc[kDecodeNT] = {};
-            row_dots<WF>(wrow, srow, xs, d, kbeg, kend, sub, nt, acc);
+            if (DOT2)
+                row_dots2<WF>(wrow, srow, xh, xpadh_len(d), kbeg, kend, sub, nt, acc);
+            else
+                row_dots<WF>(wrow, srow, xs, d, kbeg, kend, sub, nt, acc);
 #pragma unroll
             for (int q = 0; q < kDecodeNT; ++q) {
                 acc[q] += __shfl_xor(acc[q], 1, 64);
@@ -348,7 +442,8 @@ int launch_decode_gateup(const ecf_shape &s, const ExpertTables &ex, const Route
     constexpr int IB = 8, KP = 2;
     dim3 grid(s.inter / IB, maxa);
     const int ntp = std::min(kDecodeNT, T);  // an expert has at most T rows
-    const size_t sh = sizeof(float) * ntp * xpad_len(s.hidden);
+    const bool dot2 = s.a_dtype == ECF_BF16 && s.w_dtype != ECF_F32;
+    const size_t sh = dot2 ? sizeof(uint16_t) * ntp * xpadh_len(s.hidden) : sizeof(float) * ntp * xpad_len(s.hidden);
     ProfScope p("decode_gateup", st);
     const bool abf = s.a_dtype == ECF_BF16;
 #define ECF_GU(WFV, AB)                                                                             \
