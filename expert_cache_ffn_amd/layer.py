@@ -47,7 +47,12 @@ class ExpertPool:
 
 
 class Layer:
-    """One MoE layer call site: owns its workspace and builds LayerArgs."""
+    """One MoE layer call site: owns its workspace and builds LayerArgs.
+
+    LayerArgs carries raw device addresses only: every tensor passed to args()
+    must stay referenced until the forward call's work has finished on the
+    stream (a temporary such as `w.cuda()` would be freed, and its memory
+    reused, while the kernels still read it)."""
 
     def __init__(self, shape: L.Shape, max_tokens: int, device="cuda"):
         self.shape = shape

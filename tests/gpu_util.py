@@ -67,7 +67,8 @@ class Case:
         counts = torch.zeros(E, dtype=torch.int32, device="cuda")
         perm = torch.full((max(T * k, 1),), -7, dtype=torch.int32, device="cuda")
         lg_out = torch.zeros((max(T, 1), E), dtype=torch.float32, device="cuda") if self.router_w is not None else None
-        a = L.args(router_w=dev(self.router_w), router_logits=dev(self.logits), expert_ptrs=self.pool.ptrs,
+        rw, lg = dev(self.router_w), dev(self.logits)  # held: LayerArgs keeps raw addresses only
+        a = L.args(router_w=rw, router_logits=lg, expert_ptrs=self.pool.ptrs,
                    path=path, residual=residual, topk_idx=idx, topk_gate=gate, counts=counts, perm=perm,
                    logits_out=lg_out)
         st = L.forward(a, x, out)
