@@ -8,14 +8,17 @@
 // GPU after a transfer.
 //
 // Each host thread streams whole weight rows of one expert from the pinned pool
-// (bf16 widened by a shift, exact) and applies each row to all of that expert's
-// routed rows, so every weight byte is read once.  Phase 1 splits the
+// and applies each row to all of that expert's routed rows, so every weight
+// byte is read once.  Products are exact in every form (bf16 x bf16 pairs on
+// AVX-512 BF16, otherwise bf16 / E2M1 x scale widened exactly to fp32), sums
+// are fp32 with 16 or 32 independent partial sums per dot product.  Phase 1 splits the
 // gate/up rows of all host experts over the threads, phase 2 the down rows.
 #include "host_ffn.h"
 
 #include <immintrin.h>
 
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 
 namespace ecf {
@@ -104,9 +107,13 @@ enum { HF_F32 = 0, HF_BF16 = 1, HF_MX = 2 };
 
 constexpr float kE2M1[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
 
+// 2^(s - 127) built from its bits (s = 0: the subnormal 2^-127).
 inline float e8m0(uint8_t s)
 {
-    return s == 0 ? std::ldexp(1.0f, -127) : std::ldexp(1.0f, (int)s - 127);
+    const uint32_t u = s == 0 ? 0x00400000u : (uint32_t)s << 23;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
 }
 
 // Weight c of a row (scalar build).
@@ -200,16 +207,91 @@ __attribute__((target("avx2,fma"))) void dots_avx2(const void *w, const uint8_t 
     }
 }
 
-bool have_avx2()
+// AVX-512: 16-wide, two accumulators per row (32 partial sums).  bf16 weights
+// against bf16 activations use VDPBF16PS (pairs of exact bf16 products summed
+// in fp32); everything else widens the weights to fp32 and uses FMAs.  xb
+// (nullable) holds the same rows as xs in bf16.
+constexpr float kE2M1Signed[16] = {0.0f,  0.5f,  1.0f,  1.5f,  2.0f,  3.0f,  4.0f,  6.0f,
+                                   -0.0f, -0.5f, -1.0f, -1.5f, -2.0f, -3.0f, -4.0f, -6.0f};
+
+template <int WF>
+__attribute__((target("avx512f,avx512bw,avx512vl,avx512bf16"))) void dots_avx512(
+    const void *w, const uint8_t *sc, const float *const *xs, const uint16_t *const *xb, int nr, int n,
+    float *out)
 {
-    static const bool v = __builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma");
-    return v;
+    const bool dp = WF == HF_BF16 && xb != nullptr;
+    const __m512 tab = _mm512_loadu_ps(kE2M1Signed);
+    for (int r0 = 0; r0 < nr; r0 += kRowsPerDot) {
+        const int m = nr - r0 < kRowsPerDot ? nr - r0 : kRowsPerDot;
+        __m512 acc[kRowsPerDot][2];
+        for (int r = 0; r < kRowsPerDot; ++r)
+            acc[r][0] = acc[r][1] = _mm512_setzero_ps();
+        for (int c = 0; c < n; c += 32) {  // n is a multiple of 32
+            if (dp) {
+                const __m512i wv = _mm512_loadu_si512((const void *)((const uint16_t *)w + c));
+                for (int r = 0; r < m; ++r) {
+                    const __m512i xv = _mm512_loadu_si512((const void *)(xb[r0 + r] + c));
+                    acc[r][(c >> 5) & 1] = _mm512_dpbf16_ps(acc[r][(c >> 5) & 1], (__m512bh)wv, (__m512bh)xv);
+                }
+                continue;
+            }
+            __m512 wv[2];
+            if (WF == HF_MX) {
+                const __m128i bytes = _mm_loadu_si128((const __m128i *)((const uint8_t *)w + c / 2));
+                const __m128i lo = _mm_and_si128(bytes, _mm_set1_epi8(0x0f));
+                const __m128i hi = _mm_and_si128(_mm_srli_epi16(bytes, 4), _mm_set1_epi8(0x0f));
+                const __m512 scale = _mm512_set1_ps(e8m0(sc[c / 32]));
+                wv[0] = _mm512_mul_ps(_mm512_permutexvar_ps(_mm512_cvtepu8_epi32(_mm_unpacklo_epi8(lo, hi)), tab), scale);
+                wv[1] = _mm512_mul_ps(_mm512_permutexvar_ps(_mm512_cvtepu8_epi32(_mm_unpackhi_epi8(lo, hi)), tab), scale);
+            } else if (WF == HF_BF16) {
+                const __m256i a = _mm256_loadu_si256((const __m256i *)((const uint16_t *)w + c));
+                const __m256i b = _mm256_loadu_si256((const __m256i *)((const uint16_t *)w + c + 16));
+                wv[0] = _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(a), 16));
+                wv[1] = _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(b), 16));
+            } else {
+                wv[0] = _mm512_loadu_ps((const float *)w + c);
+                wv[1] = _mm512_loadu_ps((const float *)w + c + 16);
+            }
+            for (int r = 0; r < m; ++r) {
+                const float *xp = xs[r0 + r] + c;
+                acc[r][0] = _mm512_fmadd_ps(wv[0], _mm512_loadu_ps(xp), acc[r][0]);
+                acc[r][1] = _mm512_fmadd_ps(wv[1], _mm512_loadu_ps(xp + 16), acc[r][1]);
+            }
+        }
+        for (int r = 0; r < m; ++r)
+            out[r0 + r] = _mm512_reduce_add_ps(_mm512_add_ps(acc[r][0], acc[r][1]));
+    }
+}
+
+enum Isa { ISA_SCALAR = 0, ISA_AVX2 = 1, ISA_AVX512 = 2 };
+
+// The widest instruction set this CPU has (AVX-512 with BF16 dot products, else
+// AVX2 + FMA, else scalar); ECF_HOST_ISA=avx2 or =scalar asks for a narrower one.
+Isa host_isa()
+{
+    static const Isa hw = [] {
+        if (__builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw") &&
+            __builtin_cpu_supports("avx512vl") && __builtin_cpu_supports("avx512bf16"))
+            return ISA_AVX512;
+        if (__builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma"))
+            return ISA_AVX2;
+        return ISA_SCALAR;
+    }();
+    const char *e = std::getenv("ECF_HOST_ISA");
+    if (e && !std::strcmp(e, "scalar"))
+        return ISA_SCALAR;
+    if (e && !std::strcmp(e, "avx2") && hw >= ISA_AVX2)
+        return ISA_AVX2;
+    return hw;
 }
 
 template <int WF>
-void dots(const void *w, const uint8_t *sc, const float *const *xs, int nr, int n, float *out)
+void dots(Isa isa, const void *w, const uint8_t *sc, const float *const *xs, const uint16_t *const *xb, int nr,
+          int n, float *out)
 {
-    if (have_avx2())
+    if (isa == ISA_AVX512)
+        dots_avx512<WF>(w, sc, xs, xb, nr, n, out);
+    else if (isa == ISA_AVX2)
         dots_avx2<WF>(w, sc, xs, nr, n, out);
     else
         dots_scalar<WF>(w, sc, xs, nr, n, out);
@@ -229,14 +311,15 @@ inline RowRef row_of(const void *blob, size_t off_w, size_t off_s, int wf, int i
     return {b + off_w + (size_t)i * n * (wf == HF_BF16 ? 2 : 4), nullptr};
 }
 
-void dots_any(int wf, RowRef row, const float *const *xs, int nr, int n, float *out)
+void dots_any(Isa isa, int wf, RowRef row, const float *const *xs, const uint16_t *const *xb, int nr, int n,
+              float *out)
 {
     if (wf == HF_MX)
-        dots<HF_MX>(row.w, row.sc, xs, nr, n, out);
+        dots<HF_MX>(isa, row.w, row.sc, xs, xb, nr, n, out);
     else if (wf == HF_BF16)
-        dots<HF_BF16>(row.w, row.sc, xs, nr, n, out);
+        dots<HF_BF16>(isa, row.w, row.sc, xs, xb, nr, n, out);
     else
-        dots<HF_F32>(row.w, row.sc, xs, nr, n, out);
+        dots<HF_F32>(isa, row.w, row.sc, xs, xb, nr, n, out);
 }
 
 }  // namespace
@@ -248,6 +331,8 @@ int host_experts(HostPool &pool, const ecf_shape &s, const BlobLayout &lay,
         return ECF_OK;
     const int d = s.hidden, I = s.inter, k = s.top_k;
     const int wf = s.w_dtype == ECF_MXFP4 ? HF_MX : s.w_dtype == ECF_BF16 ? HF_BF16 : HF_F32;
+    const Isa isa = host_isa();
+    const bool xbf = s.a_dtype == ECF_BF16;
     // activations of every token in fp32
     std::vector<float> xf((size_t)T * d);
     if (s.a_dtype == ECF_BF16)
@@ -269,14 +354,19 @@ int host_experts(HostPool &pool, const ecf_shape &s, const BlobLayout &lay,
         const HostExpertJob &jb = jobs[task / gu_chunks];
         const int nr = (int)jb.rows.size();
         std::vector<const float *> xs(nr);
-        for (int r = 0; r < nr; ++r)
-            xs[r] = xf.data() + (size_t)(jb.rows[r] / k) * d;
+        std::vector<const uint16_t *> xb(nr);
+        for (int r = 0; r < nr; ++r) {
+            const size_t t = (size_t)(jb.rows[r] / k);
+            xs[r] = xf.data() + t * d;
+            xb[r] = xbf ? (const uint16_t *)x + t * d : nullptr;
+        }
+        const uint16_t *const *xbp = xbf ? xb.data() : nullptr;
         std::vector<float> a(nr), b(nr);
         float *hj = h.data() + hoff[task / gu_chunks];
         const int i0 = (task % gu_chunks) * CH, i1 = std::min(I, i0 + CH);
         for (int i = i0; i < i1; ++i) {
-            dots_any(wf, row_of(jb.blob, lay.off[0], lay.off[3], wf, i, d), xs.data(), nr, d, a.data());
-            dots_any(wf, row_of(jb.blob, lay.off[1], lay.off[4], wf, i, d), xs.data(), nr, d, b.data());
+            dots_any(isa, wf, row_of(jb.blob, lay.off[0], lay.off[3], wf, i, d), xs.data(), xbp, nr, d, a.data());
+            dots_any(isa, wf, row_of(jb.blob, lay.off[1], lay.off[4], wf, i, d), xs.data(), xbp, nr, d, b.data());
             for (int r = 0; r < nr; ++r)
                 hj[(size_t)r * I + i] = a[r] / (1.0f + std::exp(-a[r])) * b[r];
         }
@@ -292,7 +382,8 @@ int host_experts(HostPool &pool, const ecf_shape &s, const BlobLayout &lay,
         std::vector<float> o(nr);
         const int o0 = (task % dn_chunks) * CH, o1 = std::min(d, o0 + CH);
         for (int oo = o0; oo < o1; ++oo) {
-            dots_any(wf, row_of(jb.blob, lay.off[2], lay.off[5], wf, oo, I), hs.data(), nr, I, o.data());
+            dots_any(isa, wf, row_of(jb.blob, lay.off[2], lay.off[5], wf, oo, I), hs.data(), nullptr, nr, I,
+                     o.data());
             for (int r = 0; r < nr; ++r)
                 y[(size_t)jb.rows[r] * d + oo] = o[r];
         }

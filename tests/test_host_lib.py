@@ -202,8 +202,12 @@ def _blob(shape, tensors):
     return buf
 
 
+@pytest.mark.parametrize("isa", ["native", "avx2", "scalar"])
 @pytest.mark.parametrize("w_dtype", ["bf16", "f32", "mxfp4"])
-def test_host_experts_against_oracle(w_dtype):
+def test_host_experts_against_oracle(w_dtype, isa, monkeypatch):
+    """Every host instruction-set path (the widest the CPU has, AVX2, scalar) against the oracle."""
+    if isa != "native":
+        monkeypatch.setenv("ECF_HOST_ISA", isa)
     a_dtype = "f32" if w_dtype == "f32" else "bf16"
     cfg = syn.gen.Config(93, "t", (6,), 512, 4, 192, 2, w_dtype, a_dtype, "router")
     shape = ecf.make_shape(cfg.hidden, cfg.inter, cfg.experts, cfg.top_k, w_dtype, a_dtype)
