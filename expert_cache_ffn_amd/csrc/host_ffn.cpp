@@ -107,10 +107,11 @@ enum { HF_F32 = 0, HF_BF16 = 1, HF_MX = 2 };
 
 constexpr float kE2M1[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
 
-// 2^(s - 127) built from its bits (s = 0: the subnormal 2^-127).
+// 2^(s - 127) built from its bits (s = 0: the subnormal 2^-127; 0xFF: NaN, as
+// OCP MX v1.0 defines it).
 inline float e8m0(uint8_t s)
 {
-    const uint32_t u = s == 0 ? 0x00400000u : (uint32_t)s << 23;
+    const uint32_t u = s == 0 ? 0x00400000u : s == 255 ? 0x7FC00000u : (uint32_t)s << 23;
     float f;
     std::memcpy(&f, &u, 4);
     return f;

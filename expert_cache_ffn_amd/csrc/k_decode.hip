@@ -18,6 +18,13 @@
 
 namespace ecf {
 
+// E8M0 scale byte -> 2^(s - 127) (s = 0: the subnormal 2^-127; 0xFF: NaN, as OCP
+// MX v1.0 defines it, so the whole block's products become NaN).
+__device__ __forceinline__ float e8m0_scale(uint32_t s)
+{
+    return __uint_as_float(s == 0 ? 0x00400000u : s == 255 ? 0x7FC00000u : (s << 23));
+}
+
 // Weight formats of the GEMV path.
 enum { WF_F32 = 0, WF_BF16 = 1, WF_MX = 2 };
 
@@ -144,7 +151,7 @@ struct RowRegs {
                 break;
             const uint32_t p[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
             if (WF == WF_MX) {
-                const float sc = __uint_as_float(sb[u] == 0 ? 0x00400000u : (sb[u] << 23));
+                const float sc = e8m0_scale(sb[u]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {  // 8 elements per dword
                     const f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p[i], sc, 0);
@@ -184,7 +191,7 @@ struct RowRegs {
                 break;
             const uint32_t p[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
             if (WF == WF_MX) {
-                const float sc = __uint_as_float(sb[u] == 0 ? 0x00400000u : (sb[u] << 23));
+                const float sc = e8m0_scale(sb[u]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {  // 8 elements per dword
                     const uint32_t w[4] = {

@@ -52,9 +52,11 @@ __device__ __forceinline__ int swz(int row, int ch) { return row * 8 + (ch ^ (ro
 // rows) covers distinct bank groups.
 __device__ __forceinline__ int mx_slot(int row, int half) { return row * 2 + (half ^ (((row >> 2) ^ (row >> 3)) & 1)); }
 
+// E8M0 scale byte -> 2^(s - 127) (s = 0: the subnormal 2^-127; 0xFF: NaN, as OCP
+// MX v1.0 defines it).
 __device__ __forceinline__ float e8m0_f(uint32_t s)
 {
-    return __uint_as_float(s == 0 ? 0x00400000u : (s << 23));
+    return __uint_as_float(s == 0 ? 0x00400000u : s == 255 ? 0x7FC00000u : (s << 23));
 }
 
 // 16-byte load through a global-address-space pointer (the blob addresses come

@@ -89,7 +89,7 @@ class Case:
             lg = oracle.logits(x, self.router_w.detach().cpu())
         idx, g = oracle.route(lg, self.cfg.top_k, bool(self.renorm))
         counts, offsets, perm, pos = oracle.permute(idx, self.cfg.experts)
-        toks = np.arange(self.T) if tokens is None else np.asarray(tokens)
+        toks = np.arange(self.T) if tokens is None else np.asarray(tokens, dtype=np.int64)
         need = sorted(set(int(e) for e in idx[toks].ravel()))
         experts = [None] * self.cfg.experts
         for e in need:

@@ -193,6 +193,29 @@ def test_mxfp4_decode_and_prefill_paths_agree():
     assert np.array_equal(a["perm"], b["perm"])
 
 
+@pytest.mark.parametrize("path", [ecf.ECF_PATH_DECODE, ecf.ECF_PATH_PREFILL])
+def test_mxfp4_nan_scale_block(path):
+    """An E8M0 byte of 0xFF is NaN (OCP MX v1.0): the tokens routed to that expert
+    come out NaN in the oracle and on both GPU paths; all others stay in tolerance."""
+    cfg = cfg_small(experts=8, top_k=2, inter=256, w_dtype="mxfp4", cid=130)
+    c = Case(cfg, 24)
+    e = int(c.oracle(tokens=[])["idx"][0, 0])
+    ex = c.host_expert(e)
+    ex["s_up"][7, 2] = 255  # one scale group of up row 7
+    c.pool.load(e, {k: v.cuda() for k, v in ex.items()})
+    say(f"case: mxfp4 NaN scale in expert {e}, path {path}")
+    res = c.run(path=path)
+    ref = c.oracle()
+    got, want = res["out"], ref["out"]
+    hit = (ref["idx"] == e).any(axis=1)
+    assert hit.any() and (~hit).any()
+    assert np.isnan(want[hit]).all() and np.isfinite(want[~hit]).all()
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    tol = MX_DECODE_TOL if path == ecf.ECF_PATH_DECODE else TOL["mxfp4"]
+    rms = np.sqrt(np.mean(want[~hit] ** 2))
+    assert np.max(np.abs(got[~hit] - want[~hit])) <= tol * rms
+
+
 # ---- properties ----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("path", [ecf.ECF_PATH_DECODE, ecf.ECF_PATH_PREFILL])

@@ -250,3 +250,33 @@ def test_bandwidth_profile_argument_checks():
     assert code(host_threads=-1) == ecf.ECF_EINVAL
     assert code(d_buf_bytes=S - 1) == ecf.ECF_ENOSPC
     assert code(shape=ecf.make_shape(1000, 512, 8, 2, "bf16", "bf16")) == ecf.ECF_EINVAL
+
+
+@pytest.mark.parametrize("isa", ["native", "avx2", "scalar"])
+def test_host_experts_nan_scale_block(isa, monkeypatch):
+    """An E8M0 byte of 0xFF is NaN (OCP MX v1.0): every row routed to that expert
+    comes out NaN on the host path and in the oracle; the other rows stay exact."""
+    if isa != "native":
+        monkeypatch.setenv("ECF_HOST_ISA", isa)
+    cfg = syn.gen.Config(94, "t", (5,), 256, 4, 128, 2, "mxfp4", "bf16", "router")
+    shape = ecf.make_shape(cfg.hidden, cfg.inter, cfg.experts, cfg.top_k, "mxfp4", "bf16")
+    experts = [syn.expert_weights(cfg, 0, e) for e in range(cfg.experts)]
+    experts[2]["s_gate"][5, 3] = 255  # one scale group of gate row 5
+    blobs = [_blob(shape, ex) for ex in experts]
+    T, k = 5, cfg.top_k
+    x = syn.activations(cfg, T).contiguous()
+    idx, _ = oracle.route(syn.gen.normal(syn.key_of(94, 0, 9), T * 4).view(T, 4).float(), k)
+    rows = [[f for f in range(T * k) if idx.reshape(-1)[f] == e] for e in range(4)]
+    assert rows[2], "the test needs rows routed to expert 2"
+    y = torch.full((T * k, cfg.hidden), 7.0, dtype=torch.float32)
+    ecf.ecf_host_experts(shape, [b.data_ptr() for b in blobs], rows, x.data_ptr(), T, y.data_ptr(), 2)
+    x64 = x.double().numpy()
+    for e in range(4):
+        for f in rows[e]:
+            ref = oracle.expert_ffn(experts[e], x64[f // k], "mxfp4")
+            got = y[f].numpy()
+            assert np.array_equal(np.isnan(got), np.isnan(ref)), (e, f)
+            if e == 2:
+                assert np.isnan(ref).all()
+            else:
+                assert np.max(np.abs(got - ref)) <= 1e-5 * np.sqrt(np.mean(ref ** 2))
