@@ -340,7 +340,9 @@ static int pick_path(const ecf_layer_args *a, int32_t T)
 {
     if (a->path == ECF_PATH_DECODE || a->path == ECF_PATH_PREFILL)
         return a->path;
-    if (a->shape.w_dtype == ECF_F32)
+    // Cache mode: the decode GEMVs keep h in fp32 like the host experts, so the
+    // output does not depend on the split (the prefill GEMM rounds h to bf16).
+    if (a->cache || a->shape.w_dtype == ECF_F32)
         return ECF_PATH_DECODE;
     // bf16 and MXFP4: GEMV while each expert sees a few rows, grouped GEMM beyond
     return (T <= 64 || a->shape.inter % 128) ? ECF_PATH_DECODE : ECF_PATH_PREFILL;
@@ -543,6 +545,10 @@ int moe_layer_forward(const ecf_layer_args *a, const void *d_x, int32_t T, float
         const int path = pick_path(a, T);
         if (path == ECF_PATH_PREFILL && (s.w_dtype == ECF_F32 || s.inter % 128))
             return set_error(ECF_EUNSUPPORTED, "the prefill path needs bf16/MXFP4 weights and inter %% 128 == 0");
+        if (path == ECF_PATH_PREFILL && a->cache)
+            return set_error(ECF_EUNSUPPORTED,
+                             "cache mode runs the decode GEMVs (the prefill GEMM's bf16 h would make the "
+                             "output depend on the split)");
         hipStream_t stream = (hipStream_t)a->stream;
         char *ws = (char *)a->d_ws;
         BlobLayout lay;

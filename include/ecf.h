@@ -202,9 +202,12 @@ typedef struct {
     double b_p, b_h;             /* bandwidth figures for qstar_split (any unit, same for both) */
     int32_t q_mode;              /* ECF_Q_*: AUTO uses qstar_split; the others are for tests */
     int32_t q_fixed;             /* q for ECF_Q_FIXED (clamped to [0, m]) */
-    int32_t path;                /* ECF_PATH_*: AUTO takes the decode GEMVs for fp32 weights
-                                    and, for bf16 / MXFP4, while T <= 64 or I % 128 != 0;
-                                    the prefill grouped GEMM otherwise (bf16 / MXFP4 only) */
+    int32_t path;                /* ECF_PATH_*: AUTO takes the decode GEMVs in cache mode, for
+                                    fp32 weights and, for bf16 / MXFP4, while T <= 64 or
+                                    I % 128 != 0; the prefill grouped GEMM otherwise (bf16 /
+                                    MXFP4, all-resident only: it rounds h to bf16, the host
+                                    experts do not, so cache mode + PREFILL is
+                                    ECF_EUNSUPPORTED) */
     /* buffers */
     void *d_ws;                  /* workspace, >= ecf_workspace_bytes(shape, T) bytes, 256-B aligned */
     size_t ws_bytes;

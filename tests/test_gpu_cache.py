@@ -91,6 +91,37 @@ def test_split_invariance_small(mode, q_fixed, w_dtype):
         cs.close()
 
 
+@pytest.mark.parametrize("w_dtype", ["bf16", "mxfp4"])
+def test_split_invariance_many_tokens(w_dtype):
+    """100 tokens (past the decode/prefill switch of the all-resident mode): cache
+    mode still runs the GEMVs, so every split agrees with the resident decode
+    path within 1e-5; an explicit PREFILL request in cache mode is refused."""
+    cfg = syn.gen.Config(102, "cs", (100,), 512, 16, 256, 4, w_dtype, "bf16", "zipf", layers=1)
+    T, d = 100, cfg.hidden
+    cs = CachedSetup(cfg, 1, n_slots=6)
+    lay = Layer(cs.shape, T)
+    cstream = torch.cuda.Stream()
+    try:
+        x = syn.activations(cfg, T, device="cuda")
+        lg = syn.router_logits(cfg, T, device="cuda")
+        ref, st_ref = _run(lay, lay.args(router_logits=lg, expert_ptrs=cs.resident_ptrs[0], path=ecf.ECF_PATH_DECODE),
+                           x, T, d)
+        rms = np.sqrt(np.mean(ref ** 2))
+        for mode, qf in [(ecf.ECF_Q_ALL_HOST, 0), (ecf.ECF_Q_FIXED, 3), (ecf.ECF_Q_ALL_GPU, 0), (ecf.ECF_Q_AUTO, 0)]:
+            got, st = _run(lay, lay.args(router_logits=lg, cache=cs.cache, q_mode=mode, q_fixed=qf,
+                                         copy_stream=cstream), x, T, d)
+            err = np.max(np.abs(got - ref)) / rms
+            say(f"T=100 {w_dtype} mode {mode}: path={st['path']} m={st['misses']} q={st['q']} host={st['host']} "
+                f"err/RMS={err:.2e}")
+            assert st["path"] == ecf.ECF_PATH_DECODE
+            assert err <= SPLIT_TOL
+        with pytest.raises(ecf.EcfError) as ei:
+            _run(lay, lay.args(router_logits=lg, cache=cs.cache, path=ecf.ECF_PATH_PREFILL), x, T, d)
+        assert ei.value.code == ecf.ECF_EUNSUPPORTED
+    finally:
+        cs.close()
+
+
 def test_cache_state_invariance_and_resize():
     cfg = syn.gen.Config(101, "cs", (8,), 512, 16, 256, 4, "bf16", "bf16", "zipf", layers=2)
     L, T, d = 2, 8, cfg.hidden
