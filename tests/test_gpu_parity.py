@@ -66,6 +66,19 @@ def test_small_shapes_both_paths(path, E, k, T):
     compare(res, c.oracle(), TOL["bf16"], f"small E={E} k={k} T={T} path={path}")
 
 
+@pytest.mark.parametrize("E,k,T,path", [(1024, 32, 3, ecf.ECF_PATH_DECODE), (1024, 32, 80, ecf.ECF_PATH_DECODE),
+                                          (1024, 32, 80, ecf.ECF_PATH_PREFILL), (32, 32, 7, ecf.ECF_PATH_DECODE)])
+def test_largest_expert_count_and_topk(E, k, T, path):
+    """The declared maxima (1024 experts, top-32) and k = E: 3 tokens route in the
+    single-block kernel, 80 tokens (2,560 rows) in the multi-block counting sort."""
+    cfg = cfg_small(hidden=256, experts=E, top_k=k, inter=128, cid=140 + k + E % 7)
+    say(f"case: E={E} k={k} T={T} path={path}")
+    c = Case(cfg, T)
+    res = c.run(path=path)
+    assert res["stats"]["path"] == path
+    compare(res, c.oracle(), TOL["bf16"], f"E={E} k={k} T={T} path={path}")
+
+
 def test_tied_logits_pick_lowest_ids():
     cfg = cfg_small(logits="uniform", cid=60)
     T = 5
