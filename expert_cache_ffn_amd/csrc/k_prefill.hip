@@ -92,30 +92,25 @@ __device__ __forceinline__ bf16x8_t cvt_mx8(uint32_t w, float s)
 // One stage of global data held in registers between load and LDS store.
 // BNT = weight rows per block tile; NBL = 16-B B chunks per thread and stage.
 // A stage covers KS sub-tiles of BK = 64 reduction elements each.
-// MXFP4 weights either stay 4-bit in LDS and are expanded at every MFMA step
-// (DQ = false), or are expanded to bf16 once, when the stage is written to LDS
-// (DQ = true; the B tile is then laid out like a bf16 one).
-template <bool MX, bool DQ, int BNT, int KS>
+template <bool MX, int BNT, int KS>
 struct Stage {
     static constexpr int NBL = MX ? BNT / 128 : BNT / 32;
     u32x4_t a[4 * KS];        // A: rows (tid>>3) + 32q, chunk tid&7, per sub-tile
     u32x4_t b[NBL * KS];      // B bf16: rows (tid>>3) + 32q; MX: rows (tid>>1) + 128q, half tid&1
-    uint32_t s;               // MX, !DQ: the 2*KS scale bytes of row tid (tid < BNT)
-    uint32_t sb[MX && DQ ? NBL * KS : 1];  // MX, DQ: the scale byte of each B chunk
+    uint32_t s;               // MX: the 2*KS scale bytes of row tid (tid < BNT)
 };
 
-template <bool MX, bool DQ, int BNT>
+template <bool MX, int BNT>
 struct Ptrs {
     const char *a[4];
     const char *b[MX ? BNT / 128 : BNT / 32];
-    const uint8_t *s;                          // !DQ: scales of row tid
-    const uint8_t *sq[MX && DQ ? BNT / 128 : 1];  // DQ: scales of chunk q's row, at its half
+    const uint8_t *s;
 };
 
-template <bool MX, bool DQ, int BNT, int KS>
-__device__ __forceinline__ void gload(Stage<MX, DQ, BNT, KS> &st, const Ptrs<MX, DQ, BNT> &p, int kt, int tid)
+template <bool MX, int BNT, int KS>
+__device__ __forceinline__ void gload(Stage<MX, BNT, KS> &st, const Ptrs<MX, BNT> &p, int kt, int tid)
 {
-    constexpr int NBL = Stage<MX, DQ, BNT, KS>::NBL;
+    constexpr int NBL = Stage<MX, BNT, KS>::NBL;
 #pragma unroll
     for (int sub = 0; sub < KS; ++sub) {
         const size_t col = (size_t)(kt * KS + sub) * BK;  // first reduction element of the sub-tile
@@ -123,30 +118,25 @@ __device__ __forceinline__ void gload(Stage<MX, DQ, BNT, KS> &st, const Ptrs<MX,
         for (int q = 0; q < 4; ++q)
             st.a[sub * 4 + q] = ldg16(p.a[q] + col * 2);
 #pragma unroll
-        for (int q = 0; q < NBL; ++q) {
+        for (int q = 0; q < NBL; ++q)
             st.b[sub * NBL + q] = ldg16(p.b[q] + (MX ? col / 2 : col * 2));
-            if (MX && DQ)
-                st.sb[sub * NBL + q] = ldg1(p.sq[q] + col / 32);
-        }
     }
     // every thread loads (threads past BNT re-read row 0's scales), so the number
     // of loads in flight is the same on every path and the compiler's load
     // counters can wait for exactly the older stage
-    if (MX && !DQ)
+    if (MX)
         st.s = KS == 2 ? ldg4(p.s + (size_t)kt * 4) : ldg2(p.s + (size_t)kt * 2);
 }
 
 // Registers -> LDS.  Sub-tile `sub` of A sits at As + sub * BM * 8 and of B at
-// Bs + sub * (B tile size).  MX, !DQ: scales are widened to fp32 here, once per
-// row and stage, and stored group-major: Scf[group * (BNT + 32) + row] (the pad
-// puts the two lane halves' reads on different banks).  MX, DQ: each thread
-// expands its 32 weights (one scale group) to four bf16 chunks.
-template <bool MX, bool DQ, int BNT, int KS>
-__device__ __forceinline__ void sstore(const Stage<MX, DQ, BNT, KS> &st, u32x4_t *As, u32x4_t *Bs, float *Scf,
-                                       int tid)
+// Bs + sub * (B tile size).  MX scales are widened to fp32 here, once per row
+// and stage, and stored group-major: Scf[group * (BNT + 32) + row] (the pad
+// puts the two lane halves' reads on different banks).
+template <bool MX, int BNT, int KS>
+__device__ __forceinline__ void sstore(const Stage<MX, BNT, KS> &st, u32x4_t *As, u32x4_t *Bs, float *Scf, int tid)
 {
-    constexpr int NBL = Stage<MX, DQ, BNT, KS>::NBL;
-    constexpr int BT = MX && !DQ ? BNT * 2 : BNT * 8;  // 16-B slots of one B sub-tile
+    constexpr int NBL = Stage<MX, BNT, KS>::NBL;
+    constexpr int BT = MX ? BNT * 2 : BNT * 8;  // 16-B slots of one B sub-tile
 #pragma unroll
     for (int sub = 0; sub < KS; ++sub) {
 #pragma unroll
@@ -154,21 +144,13 @@ __device__ __forceinline__ void sstore(const Stage<MX, DQ, BNT, KS> &st, u32x4_t
             As[sub * BM * 8 + swz((tid >> 3) + 32 * q, tid & 7)] = st.a[sub * 4 + q];
 #pragma unroll
         for (int q = 0; q < NBL; ++q) {
-            if (MX && DQ) {
-                const int row = (tid >> 1) + 128 * q, h = tid & 1;
-                const float sc = e8m0_f(st.sb[sub * NBL + q]);
-                const u32x4_t w = st.b[sub * NBL + q];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    Bs[sub * BT + swz(row, 4 * h + i)] = __builtin_bit_cast(u32x4_t, cvt_mx8(w[i], sc));
-            } else if (MX) {
+            if (MX)
                 Bs[sub * BT + mx_slot((tid >> 1) + 128 * q, tid & 1)] = st.b[sub * NBL + q];
-            } else {
+            else
                 Bs[sub * BT + swz((tid >> 3) + 32 * q, tid & 7)] = st.b[sub * NBL + q];
-            }
         }
     }
-    if (MX && !DQ && (BNT >= 256 || tid < BNT)) {
+    if (MX && (BNT >= 256 || tid < BNT)) {
 #pragma unroll
         for (int gi = 0; gi < 2 * KS; ++gi)
             Scf[gi * (BNT + 32) + tid] = e8m0_f((st.s >> (8 * gi)) & 0xffu);
@@ -202,7 +184,7 @@ struct IC {
 // and B alike, so every chunk is used once.  Lane half g then reads the 32
 // MXFP4 elements 32g..32g+31 -- 16 bytes, exactly one E8M0 scale group -- with
 // a single LDS read per k-tile.
-template <int MODE, bool MX, int BNT, int MINB, int KS, int WM, bool DQ>
+template <int MODE, bool MX, int BNT, int MINB, int KS, int WM>
 __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
     const uint64_t *__restrict__ ptrs, size_t off_w0, size_t off_w1, size_t off_s0, size_t off_s1,
     const int32_t *__restrict__ tiles, const int32_t *__restrict__ n_tiles,
@@ -210,11 +192,10 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
     int K, int N, int lda, int k, int E, int R, int NT, void *__restrict__ out)
 {
     constexpr int NCB = BNT / 64;  // 32-column MFMA blocks per wave
-    constexpr bool MXL = MX && !DQ;  // 4-bit weights in LDS, expanded per MFMA step
-    constexpr int BT = MXL ? BNT * 2 : BNT * 8;  // 16-B slots of one B sub-tile
+    constexpr int BT = MX ? BNT * 2 : BNT * 8;  // 16-B slots of one B sub-tile
     __shared__ u32x4_t As[2][KS * BM * 8];
     __shared__ u32x4_t Bs[2][KS * BT];
-    __shared__ float Scf[2][MXL ? 2 * KS * (BNT + 32) : 4];
+    __shared__ float Scf[2][MX ? 2 * KS * (BNT + 32) : 4];
 
     const int item = xcd_item(blockIdx.x, *n_tiles * NT);
     if (item < 0)
@@ -235,7 +216,7 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
     // MODE 1: this block's intermediate columns [n0, n0 + BNT/2); MODE 2: outputs [n0, n0 + BNT)
     const int n0 = nt * (MODE == 1 ? BNT / 2 : BNT);
 
-    Ptrs<MX, DQ, BNT> p;
+    Ptrs<MX, BNT> p;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int row = min((tid >> 3) + 32 * q, mrows - 1);
@@ -259,8 +240,6 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
             size_t so, sco;
             const int r = brow((tid >> 1) + 128 * q, so, sco);
             p.b[q] = (const char *)blob + so + (size_t)r * (K / 2) + (tid & 1) * 16;
-            if (DQ)
-                p.sq[MX && DQ ? q : 0] = (const uint8_t *)blob + sco + (size_t)r * (K / 32) + (tid & 1);
         }
         size_t so, sco;
         const int r = brow(tid < BNT ? tid : 0, so, sco);
@@ -295,10 +274,10 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
 #pragma unroll
                 for (int j = 0; j < 16; ++j)
                     acc[a][b][j] = 0.f;
-        Stage<MX, DQ, BNT, KS> s0, s1;
-        gload<MX, DQ, BNT, KS>(s0, p, 0, tid);
-        gload<MX, DQ, BNT, KS>(s1, p, 1, tid);
-        sstore<MX, DQ, BNT, KS>(s0, As[0], Bs[0], Scf[0], tid);
+        Stage<MX, BNT, KS> s0, s1;
+        gload<MX, BNT, KS>(s0, p, 0, tid);
+        gload<MX, BNT, KS>(s1, p, 1, tid);
+        sstore<MX, BNT, KS>(s0, As[0], Bs[0], Scf[0], tid);
         __syncthreads();
         // NXT holds k-tile kt+1 (loaded one iteration ago); FRE is free and
         // receives k-tile kt+2.  Two copies of the body alternate the roles so
@@ -310,13 +289,13 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
 #define ECF_GEMM_BODY(KT, NXT, FRE)                                                                  \
     {                                                                                               \
         const int cur = (KT) & 1;                                                                   \
-        gload<MX, DQ, BNT, KS>(FRE, p, min((KT) + 2, nk - 1), tid);                                 \
+        gload<MX, BNT, KS>(FRE, p, min((KT) + 2, nk - 1), tid);                                     \
         if (NMS > 0) {                                                                              \
             _Pragma("unroll") for (int sub = 0; sub < KS; ++sub)                                    \
             {                                                                                       \
                 const u32x4_t *Asb = As[cur] + sub * BM * 8, *Bsb = Bs[cur] + sub * BT;             \
                 float bsc[NCB];                                                                     \
-                if (MXL) {                                                                          \
+                if (MX) {                                                                           \
                     _Pragma("unroll") for (int cb = 0; cb < NCB; ++cb)                              \
                         bsc[cb] = Scf[cur][(sub * 2 + g) * (BNT + 32) + brw[cb]];                   \
                 }                                                                                   \
@@ -327,16 +306,16 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
                     _Pragma("unroll") for (int ms = 0; ms < NMS; ++ms) af[ms] =                    \
                         frag_bf16(Asb, wm * WROWS + ms * 32 + (l & 31), kc);                        \
                     _Pragma("unroll") for (int cb = 0; cb < NCB; ++cb) bfr[cb] =                    \
-                        MXL ? cvt_mx8(reinterpret_cast<const uint32_t *>(Bsb)[mx_slot(brw[cb], g) * 4 + ks], \
+                        MX ? cvt_mx8(reinterpret_cast<const uint32_t *>(Bsb)[mx_slot(brw[cb], g) * 4 + ks], \
                                      bsc[cb])                                                       \
-                            : frag_bf16(Bsb, brw[cb], kc);                                          \
+                           : frag_bf16(Bsb, brw[cb], kc);                                           \
                     _Pragma("unroll") for (int ms = 0; ms < NMS; ++ms)                              \
                         _Pragma("unroll") for (int cb = 0; cb < NCB; ++cb) acc[ms][cb] =            \
                             __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ms], bfr[cb], acc[ms][cb], 0, 0, 0); \
                 }                                                                                   \
             }                                                                                       \
         }                                                                                           \
-        sstore<MX, DQ, BNT, KS>(NXT, As[cur ^ 1], Bs[cur ^ 1], Scf[cur ^ 1], tid);                  \
+        sstore<MX, BNT, KS>(NXT, As[cur ^ 1], Bs[cur ^ 1], Scf[cur ^ 1], tid);                      \
         __syncthreads();                                                                            \
     }
         for (int kt = 0; kt < nk; kt += 2) {
@@ -393,7 +372,7 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
 // per CU, one 64-wide sub-tile per stage, 2 x 2 waves; 128 weight rows per
 // N-tile for bf16 (HBM-bound there), 256 for MXFP4 (halves the A re-reads and
 // the per-row MFMA overheads).  Two-sub-tile stages, a 1 x 4 wave layout, three
-// blocks per CU and expanding MXFP4 to bf16 at the LDS store (DQ) were each
+// blocks per CU and expanding MXFP4 to bf16 once at the LDS store were each
 // slower or spilled registers.
 #ifndef ECF_BF16_BNT
 #define ECF_BF16_BNT 128
@@ -407,9 +386,6 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
 #define ECF_MX_KS 1
 #define ECF_MX_WM 2
 #endif
-#ifndef ECF_MX_DQ
-#define ECF_MX_DQ false
-#endif
 
 int launch_prefill_gemm1(const ecf_shape &s, const ExpertTables &ex, const RouteOut &o, const void *x,
                          int T, uint16_t *H, hipStream_t st)
@@ -420,7 +396,7 @@ int launch_prefill_gemm1(const ecf_shape &s, const ExpertTables &ex, const Route
     const int nblk = max_tiles(s, T) * NT;
     ProfScope p("prefill_gemm1", st);
 #define ECF_G1(MXV, BNV, MBV, KSV, WMV)                                                                    \
-    hipLaunchKernelGGL((k_grouped_gemm<1, MXV, BNV, MBV, KSV, WMV, (MXV) && ECF_MX_DQ>), dim3(nblk), dim3(256), 0, st, ex.ptrs,  \
+    hipLaunchKernelGGL((k_grouped_gemm<1, MXV, BNV, MBV, KSV, WMV>), dim3(nblk), dim3(256), 0, st, ex.ptrs,  \
                        ex.lay.off[0], ex.lay.off[1], ex.lay.off[3], ex.lay.off[4], o.tiles, o.n_tiles,         \
                        o.offsets, o.perm, (const uint16_t *)x, s.hidden, s.inter, s.hidden, s.top_k,         \
                        s.n_experts, T * s.top_k, NT, (void *)H)
@@ -444,7 +420,7 @@ int launch_prefill_gemm2(const ecf_shape &s, const ExpertTables &ex, const Route
     const int nblk = max_tiles(s, T) * NT;
     ProfScope p("prefill_gemm2", st);
 #define ECF_G2(MXV, BNV, MBV, KSV, WMV)                                                                    \
-    hipLaunchKernelGGL((k_grouped_gemm<2, MXV, BNV, MBV, KSV, WMV, (MXV) && ECF_MX_DQ>), dim3(nblk), dim3(256), 0, st, ex.ptrs,  \
+    hipLaunchKernelGGL((k_grouped_gemm<2, MXV, BNV, MBV, KSV, WMV>), dim3(nblk), dim3(256), 0, st, ex.ptrs,  \
                        ex.lay.off[2], ex.lay.off[2], ex.lay.off[5], ex.lay.off[5], o.tiles, o.n_tiles,         \
                        o.offsets, o.perm, H, s.inter, s.hidden, s.inter, s.top_k, s.n_experts, T * s.top_k,  \
                        NT, (void *)Y)
