@@ -251,19 +251,21 @@ size_t ecf_workspace_bytes(const ecf_shape *shape, int32_t max_tokens)
 int prefetch_layer(const void *h_layer_blob, void *d_buf, size_t bytes, size_t buf_capacity,
                    void *copy_stream, void *done_event)
 {
-    if (!h_layer_blob || !d_buf)
-        return set_error(ECF_EINVAL, "prefetch_layer: NULL buffer");
-    if (bytes > buf_capacity)
-        return set_error(ECF_ENOSPC, "prefetch_layer: %zu bytes do not fit a %zu-byte buffer", bytes,
-                         buf_capacity);
-    hipStream_t st = (hipStream_t)copy_stream;
-    {
-        ProfScope p("prefetch_layer_copy", st);
-        ECF_HIP_CHECK(hipMemcpyAsync(d_buf, h_layer_blob, bytes, hipMemcpyHostToDevice, st));
-    }
-    if (done_event)
-        ECF_HIP_CHECK(hipEventRecord((hipEvent_t)done_event, st));
-    return ECF_OK;
+    return ::ecf::guarded("prefetch_layer", [&]() -> int {
+        if (!h_layer_blob || !d_buf)
+            return set_error(ECF_EINVAL, "prefetch_layer: NULL buffer");
+        if (bytes > buf_capacity)
+            return set_error(ECF_ENOSPC, "prefetch_layer: %zu bytes do not fit a %zu-byte buffer", bytes,
+                             buf_capacity);
+        hipStream_t st = (hipStream_t)copy_stream;
+        {
+            ProfScope p("prefetch_layer_copy", st);
+            ECF_HIP_CHECK(hipMemcpyAsync(d_buf, h_layer_blob, bytes, hipMemcpyHostToDevice, st));
+        }
+        if (done_event)
+            ECF_HIP_CHECK(hipEventRecord((hipEvent_t)done_event, st));
+        return ECF_OK;
+    });
 }
 
 int ecf_host_experts(const ecf_shape *shape, int32_t n_jobs, const void *const *h_blobs,
@@ -304,34 +306,40 @@ int ecf_host_experts(const ecf_shape *shape, int32_t n_jobs, const void *const *
 
 int ecf_profile_enable(int32_t on)
 {
-    std::lock_guard<std::mutex> g(g_prof_mu);
-    g_prof_on = on != 0;
-    return ECF_OK;
+    return ::ecf::guarded("ecf_profile_enable", [&]() -> int {
+        std::lock_guard<std::mutex> g(g_prof_mu);
+        g_prof_on = on != 0;
+        return ECF_OK;
+    });
 }
 
 int ecf_profile_get(int32_t i, const char **name, int64_t *launches, double *total_ms)
 {
-    const int rc = prof_resolve();
-    if (rc != ECF_OK)
-        return rc;
-    std::lock_guard<std::mutex> g(g_prof_mu);
-    if (i < 0 || i >= (int32_t)g_prof.size())
-        return set_error(ECF_EINVAL, "ecf_profile_get: no entry %d", i);
-    if (name)
-        *name = g_prof[i].name.c_str();
-    if (launches)
-        *launches = g_prof[i].n;
-    if (total_ms)
-        *total_ms = g_prof[i].ms;
-    return ECF_OK;
+    return ::ecf::guarded("ecf_profile_get", [&]() -> int {
+        const int rc = prof_resolve();
+        if (rc != ECF_OK)
+            return rc;
+        std::lock_guard<std::mutex> g(g_prof_mu);
+        if (i < 0 || i >= (int32_t)g_prof.size())
+            return set_error(ECF_EINVAL, "ecf_profile_get: no entry %d", i);
+        if (name)
+            *name = g_prof[i].name.c_str();
+        if (launches)
+            *launches = g_prof[i].n;
+        if (total_ms)
+            *total_ms = g_prof[i].ms;
+        return ECF_OK;
+    });
 }
 
 int ecf_profile_reset(void)
 {
-    const int rc = prof_resolve();
-    std::lock_guard<std::mutex> g(g_prof_mu);
-    g_prof.clear();
-    return rc;
+    return ::ecf::guarded("ecf_profile_reset", [&]() -> int {
+        const int rc = prof_resolve();
+        std::lock_guard<std::mutex> g(g_prof_mu);
+        g_prof.clear();
+        return rc;
+    });
 }
 
 // ---------------------------------------------------------------------------------------

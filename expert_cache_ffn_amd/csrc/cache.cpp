@@ -93,31 +93,33 @@ void ecf_cache_destroy(ecf_cache *c)
 
 int expert_cache_lookup(ecf_cache *c, int32_t layer, const int32_t *experts, int32_t n, int32_t *slots)
 {
-    if (!c || layer < 0 || layer >= c->L || n < 0 || (n > 0 && (!experts || !slots)))
-        return set_error(ECF_EINVAL, "expert_cache_lookup: bad arguments");
-    for (int32_t i = 0; i < n; ++i)
-        if (experts[i] < 0 || experts[i] >= c->E)
-            return set_error(ECF_EINVAL, "expert_cache_lookup: expert %d out of range", experts[i]);
-    ++c->gen;
-    c->n_pinned = 0;
-    c->step_layer = layer;
-    for (int32_t i = 0; i < n; ++i) {
-        const int32_t s = c->slot_of[key_of(c, layer, experts[i])];
-        ++c->stats.lookups;
-        slots[i] = s;
-        if (s < 0) {
-            ++c->stats.misses;
-            continue;
+    return ::ecf::guarded("expert_cache_lookup", [&]() -> int {
+        if (!c || layer < 0 || layer >= c->L || n < 0 || (n > 0 && (!experts || !slots)))
+            return set_error(ECF_EINVAL, "expert_cache_lookup: bad arguments");
+        for (int32_t i = 0; i < n; ++i)
+            if (experts[i] < 0 || experts[i] >= c->E)
+                return set_error(ECF_EINVAL, "expert_cache_lookup: expert %d out of range", experts[i]);
+        ++c->gen;
+        c->n_pinned = 0;
+        c->step_layer = layer;
+        for (int32_t i = 0; i < n; ++i) {
+            const int32_t s = c->slot_of[key_of(c, layer, experts[i])];
+            ++c->stats.lookups;
+            slots[i] = s;
+            if (s < 0) {
+                ++c->stats.misses;
+                continue;
+            }
+            ++c->stats.hits;
+            unlink(c, s);
+            push_mru(c, s);
+            if (!pinned(c, s)) {
+                c->pin_gen[s] = c->gen;
+                ++c->n_pinned;
+            }
         }
-        ++c->stats.hits;
-        unlink(c, s);
-        push_mru(c, s);
-        if (!pinned(c, s)) {
-            c->pin_gen[s] = c->gen;
-            ++c->n_pinned;
-        }
-    }
-    return ECF_OK;
+        return ECF_OK;
+    });
 }
 
 int32_t ecf_cache_available(const ecf_cache *c)
@@ -130,54 +132,56 @@ int32_t ecf_cache_available(const ecf_cache *c)
 int expert_cache_evict(ecf_cache *c, int32_t layer, const int32_t *experts, int32_t n, int32_t *slots,
                        int32_t *victims)
 {
-    if (!c || n < 0 || (n > 0 && (!experts || !slots)))
-        return set_error(ECF_EINVAL, "expert_cache_evict: bad arguments");
-    if (c->step_layer < 0 || layer != c->step_layer)
-        return set_error(ECF_ESTATE, "expert_cache_evict: layer %d has no open layer-step (lookup first)",
-                         layer);
-    for (int32_t i = 0; i < n; ++i) {
-        if (experts[i] < 0 || experts[i] >= c->E)
-            return set_error(ECF_EINVAL, "expert_cache_evict: expert %d out of range", experts[i]);
-        if (c->slot_of[key_of(c, layer, experts[i])] >= 0)
-            return set_error(ECF_EINVAL, "expert_cache_evict: expert %d already resident", experts[i]);
-        for (int32_t j = 0; j < i; ++j)
-            if (experts[j] == experts[i])
-                return set_error(ECF_EINVAL, "expert_cache_evict: expert %d repeated", experts[i]);
-    }
-    if (n > ecf_cache_available(c))
-        return set_error(ECF_ENOSPC, "expert_cache_evict: %d slots wanted, %d available", n,
-                         ecf_cache_available(c));
-    for (int32_t i = 0; i < n; ++i) {
-        int32_t s, victim = -1;
-        if (!c->free.empty()) {
-            s = *c->free.begin();
-            c->free.erase(c->free.begin());
-        } else {
-            s = c->head;
-            while (s >= 0 && pinned(c, s))
-                s = c->next[s];
-            if (s < 0)  // cannot happen: availability was checked
-                return set_error(ECF_ESTATE, "expert_cache_evict: no evictable slot");
-            const int64_t old = c->key_of_slot[s];
-            c->slot_of[old] = -1;
-            unlink(c, s);
-            --c->n_resident;
-            victim = (int32_t)old;
-            ++c->stats.evictions;
+    return ::ecf::guarded("expert_cache_evict", [&]() -> int {
+        if (!c || n < 0 || (n > 0 && (!experts || !slots)))
+            return set_error(ECF_EINVAL, "expert_cache_evict: bad arguments");
+        if (c->step_layer < 0 || layer != c->step_layer)
+            return set_error(ECF_ESTATE, "expert_cache_evict: layer %d has no open layer-step (lookup first)",
+                             layer);
+        for (int32_t i = 0; i < n; ++i) {
+            if (experts[i] < 0 || experts[i] >= c->E)
+                return set_error(ECF_EINVAL, "expert_cache_evict: expert %d out of range", experts[i]);
+            if (c->slot_of[key_of(c, layer, experts[i])] >= 0)
+                return set_error(ECF_EINVAL, "expert_cache_evict: expert %d already resident", experts[i]);
+            for (int32_t j = 0; j < i; ++j)
+                if (experts[j] == experts[i])
+                    return set_error(ECF_EINVAL, "expert_cache_evict: expert %d repeated", experts[i]);
         }
-        const int64_t key = key_of(c, layer, experts[i]);
-        c->slot_of[key] = s;
-        c->key_of_slot[s] = key;
-        push_mru(c, s);
-        ++c->n_resident;
-        c->pin_gen[s] = c->gen;
-        ++c->n_pinned;
-        ++c->stats.inserts;
-        slots[i] = s;
-        if (victims)
-            victims[i] = victim;
-    }
-    return ECF_OK;
+        if (n > ecf_cache_available(c))
+            return set_error(ECF_ENOSPC, "expert_cache_evict: %d slots wanted, %d available", n,
+                             ecf_cache_available(c));
+        for (int32_t i = 0; i < n; ++i) {
+            int32_t s, victim = -1;
+            if (!c->free.empty()) {
+                s = *c->free.begin();
+                c->free.erase(c->free.begin());
+            } else {
+                s = c->head;
+                while (s >= 0 && pinned(c, s))
+                    s = c->next[s];
+                if (s < 0)  // cannot happen: availability was checked
+                    return set_error(ECF_ESTATE, "expert_cache_evict: no evictable slot");
+                const int64_t old = c->key_of_slot[s];
+                c->slot_of[old] = -1;
+                unlink(c, s);
+                --c->n_resident;
+                victim = (int32_t)old;
+                ++c->stats.evictions;
+            }
+            const int64_t key = key_of(c, layer, experts[i]);
+            c->slot_of[key] = s;
+            c->key_of_slot[s] = key;
+            push_mru(c, s);
+            ++c->n_resident;
+            c->pin_gen[s] = c->gen;
+            ++c->n_pinned;
+            ++c->stats.inserts;
+            slots[i] = s;
+            if (victims)
+                victims[i] = victim;
+        }
+        return ECF_OK;
+    });
 }
 
 int32_t ecf_cache_slot_of(const ecf_cache *c, int32_t layer, int32_t expert)
@@ -189,35 +193,39 @@ int32_t ecf_cache_slot_of(const ecf_cache *c, int32_t layer, int32_t expert)
 
 int ecf_cache_get_stats(const ecf_cache *c, ecf_cache_stats *out)
 {
-    if (!c || !out)
-        return set_error(ECF_EINVAL, "ecf_cache_get_stats: NULL argument");
-    *out = c->stats;
-    return ECF_OK;
+    return ::ecf::guarded("ecf_cache_get_stats", [&]() -> int {
+        if (!c || !out)
+            return set_error(ECF_EINVAL, "ecf_cache_get_stats: NULL argument");
+        *out = c->stats;
+        return ECF_OK;
+    });
 }
 
 int ecf_cache_resize(ecf_cache *c, int32_t n_slots)
 {
-    if (!c || n_slots < 0 || n_slots > c->max_slots)
-        return set_error(ECF_EINVAL, "ecf_cache_resize: n_slots must be in [0, max_slots]");
-    for (int32_t s = n_slots; s < c->n_slots; ++s) {
-        c->free.erase(s);
-        const int64_t key = c->key_of_slot[s];
-        if (key >= 0) {
-            c->slot_of[key] = -1;
-            c->key_of_slot[s] = -1;
-            unlink(c, s);
-            --c->n_resident;
-            if (pinned(c, s))
-                --c->n_pinned;
-            c->pin_gen[s] = 0;
-            ++c->stats.dropped;
+    return ::ecf::guarded("ecf_cache_resize", [&]() -> int {
+        if (!c || n_slots < 0 || n_slots > c->max_slots)
+            return set_error(ECF_EINVAL, "ecf_cache_resize: n_slots must be in [0, max_slots]");
+        for (int32_t s = n_slots; s < c->n_slots; ++s) {
+            c->free.erase(s);
+            const int64_t key = c->key_of_slot[s];
+            if (key >= 0) {
+                c->slot_of[key] = -1;
+                c->key_of_slot[s] = -1;
+                unlink(c, s);
+                --c->n_resident;
+                if (pinned(c, s))
+                    --c->n_pinned;
+                c->pin_gen[s] = 0;
+                ++c->stats.dropped;
+            }
         }
-    }
-    for (int32_t s = c->n_slots; s < n_slots; ++s)
-        c->free.insert(s);
-    c->n_slots = n_slots;
-    c->step_layer = -1;  // a resize is a safe point: no layer-step stays open
-    return ECF_OK;
+        for (int32_t s = c->n_slots; s < n_slots; ++s)
+            c->free.insert(s);
+        c->n_slots = n_slots;
+        c->step_layer = -1;  // a resize is a safe point: no layer-step stays open
+        return ECF_OK;
+    });
 }
 
 }  // extern "C"

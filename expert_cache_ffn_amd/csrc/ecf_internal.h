@@ -1,6 +1,8 @@
 // Internal declarations shared by the host-side sources of libecf.
 #pragma once
 
+#include <new>
+
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -13,6 +15,20 @@ namespace ecf {
 
 // ---- errors -------------------------------------------------------------------
 int set_error(int code, const char *fmt, ...);
+// Runs an entry point's body; no exception crosses the C ABI (host memory
+// exhaustion -> ECF_ENOSPC, anything else -> ECF_EINVAL).
+template <class F>
+int guarded(const char *name, F &&f) noexcept
+{
+    try {
+        return f();
+    } catch (const std::bad_alloc &) {
+        return set_error(ECF_ENOSPC, "%s: out of host memory", name);
+    } catch (...) {
+        return set_error(ECF_EINVAL, "%s: internal failure", name);
+    }
+}
+
 #define ECF_HIP_CHECK(expr)                                                                   \
     do {                                                                                      \
         hipError_t _e = (expr);                                                               \
