@@ -50,6 +50,38 @@ def src_hash(*names):
     return h.hexdigest()[:16]
 
 
+# ---- achievable HBM bandwidth on this GPU (context for the roofline's 8 TB/s peak) ----------
+
+def bench_hbm(torch, ecf, reps=10):
+    """A plain streaming read of 4 GiB (libecf's ecf_stream_read: 16 B per lane,
+    eight loads in flight) and a 2 GiB device copy (torch), timed with HIP
+    events: what simple kernels reach on this GPU."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.float32, device="cuda")  # contents do not matter for timing
+    b = torch.empty(n // 2, dtype=torch.float32, device="cuda")
+    c = torch.empty_like(b)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    out = {}
+    read = lambda: ecf.ecf_stream_read(a.data_ptr(), 4 * n, sink.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    for name, fn, nbytes in (("read", read, 4 * n), ("copy", lambda: c.copy_(b), 2 * 4 * (n // 2))):
+        fn()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(reps):
+            fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        out[f"{name}_GBps"] = nbytes * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    del a, b, c, sink
+    torch.cuda.empty_cache()
+    out["peak_GBps"] = HBM_PEAK_GBS
+    log(f"hbm: plain read {out['read_GBps']:.0f} GB/s, device copy {out['copy_GBps']:.0f} GB/s "
+        f"(read+write), datasheet peak {HBM_PEAK_GBS:.0f}")
+    return out
+
+
 # ---- decode (headline) ---------------------------------------------------------------
 
 def bench_decode(torch, ecf, syn, Ts, steps, warmup, n_batches=64, use_graph=True, host_inputs=False,
@@ -489,8 +521,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workloads",
-                    default="decode,decode_fp4,prefill,prefill_fp4,prefetch,cached,bandwidth,policies,cached_fp4",
-                    help="any of decode, decode_fp4, prefill, prefill_fp4, prefetch, cached, bandwidth, policies, "
+                    default="hbm,decode,decode_fp4,prefill,prefill_fp4,prefetch,cached,bandwidth,policies,cached_fp4",
+                    help="any of hbm, decode, decode_fp4, prefill, prefill_fp4, prefetch, cached, bandwidth, policies, "
                          "cached_fp4 (policies: the cached-decode policy ablation at equal capacity; *_fp4: the "
                          "same layers with MXFP4 experts)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -524,6 +556,7 @@ def main():
         log("calibration copy: 1 GiB device to device")
         del src, dst
     wl = set(args.workloads.split(","))
+    hbm = bench_hbm(torch, ecf) if "hbm" in wl else None
     Ts = tuple(int(t) for t in args.decode_tokens.split(","))
     head, also, cpu, sample = None, {}, None, None
     if "decode" in wl:
@@ -610,7 +643,8 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": head["gateup_GBps"] / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": head["gateup_bytes"],
                      "avg_launch_us": head["gateup_avg_us"],
-                     "whole_layer_GBps": head["layer_GBps"], "whole_layer_frac": head["layer_hbm_frac"]},
+                     "whole_layer_GBps": head["layer_GBps"], "whole_layer_frac": head["layer_hbm_frac"],
+                     "achievable_on_this_gpu": hbm},
         "cpu_baseline": cpu,
         "also": also,
         "headline_detail": head,

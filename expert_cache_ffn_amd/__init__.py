@@ -19,5 +19,5 @@ from ._lib import (  # noqa: F401
     ecf_cache_create, ecf_cache_destroy, expert_cache_lookup, expert_cache_evict,
     ecf_cache_available, ecf_cache_slot_of, ecf_cache_get_stats, ecf_cache_resize,
     prefetch_layer, moe_layer_forward, ecf_host_experts, ecf_bandwidth_profile,
-    ecf_profile_enable, ecf_profile_get_all, ecf_profile_reset,
+    ecf_profile_enable, ecf_profile_get_all, ecf_profile_reset, ecf_stream_read,
 )

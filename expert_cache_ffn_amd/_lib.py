@@ -25,7 +25,7 @@ EXPORTS = [
     "ecf_cache_create", "ecf_cache_destroy", "expert_cache_lookup", "expert_cache_evict",
     "ecf_cache_available", "ecf_cache_slot_of", "ecf_cache_get_stats", "ecf_cache_resize",
     "prefetch_layer", "moe_layer_forward", "ecf_host_experts", "ecf_bandwidth_profile", "ecf_profile_enable",
-    "ecf_profile_get", "ecf_profile_reset",
+    "ecf_profile_get", "ecf_profile_reset", "ecf_stream_read",
 ]
 
 
@@ -120,6 +120,8 @@ def lib():
         L.ecf_profile_get.argtypes = [c_int32, POINTER(c_char_p), POINTER(c_int64), POINTER(c_double)]
         L.ecf_profile_get.restype = c_int32
         L.ecf_profile_reset.argtypes, L.ecf_profile_reset.restype = [], c_int32
+        L.ecf_stream_read.argtypes = [c_void_p, c_size_t, c_void_p, c_void_p]
+        L.ecf_stream_read.restype = c_int32
         _lib = L
     return _lib
 
@@ -265,6 +267,10 @@ def ecf_profile_get_all() -> dict:
         out[name.value.decode()] = (n.value, ms.value)
         i += 1
     return out
+
+
+def ecf_stream_read(d_buf, nbytes, d_sink, stream=0):
+    return _check(lib().ecf_stream_read(int(d_buf) or None, int(nbytes), int(d_sink) or None, int(stream) or None))
 
 
 def ecf_profile_reset():

@@ -287,6 +287,15 @@ int ecf_profile_enable(int32_t on);
 int ecf_profile_get(int32_t i, const char **name, int64_t *launches, double *total_ms);
 int ecf_profile_reset(void);
 
+/*
+ * One plain streaming read of bytes (a multiple of 16) at d_buf (16-byte
+ * aligned), 16 bytes per lane and load, as a yardstick for the HBM bandwidth the
+ * layer's kernels reach; *d_sink ^= the XOR of every 32-bit word read (the
+ * caller zeroes it first if it wants the value).  Asynchronous on stream (NULL =
+ * null stream); the caller times it.  ECF_EINVAL for bad pointers or sizes.
+ */
+int ecf_stream_read(const void *d_buf, size_t bytes, uint32_t *d_sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

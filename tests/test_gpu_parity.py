@@ -280,3 +280,17 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy(), eager), f"replay {rep} differs"
         del junk
+
+
+def test_stream_read_xor():
+    """The bandwidth yardstick reads every word exactly once (XOR of all words)."""
+    import numpy as np
+    rng = np.random.default_rng(5)
+    for n_words in (4, 1000, (1 << 20) + 12):
+        words = rng.integers(0, 2 ** 32, size=n_words, dtype=np.uint64).astype(np.uint32)
+        buf = torch.from_numpy(words.view(np.int32)).cuda()
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        ecf.ecf_stream_read(buf.data_ptr(), 4 * n_words, sink.data_ptr())
+        torch.cuda.synchronize()
+        assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(np.bitwise_xor.reduce(words))

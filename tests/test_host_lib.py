@@ -280,3 +280,11 @@ def test_host_experts_nan_scale_block(isa, monkeypatch):
                 assert np.isnan(ref).all()
             else:
                 assert np.max(np.abs(got - ref)) <= 1e-5 * np.sqrt(np.mean(ref ** 2))
+
+
+def test_stream_read_argument_checks():
+    """Rejected before any HIP call: unaligned buffer, size not a multiple of 16, NULL sink."""
+    for buf, n, sink in ((4096 + 4, 64, 8192), (4096, 60, 8192), (4096, 64, 0), (0, 64, 8192)):
+        with pytest.raises(ecf.EcfError) as ei:
+            ecf.ecf_stream_read(buf, n, sink)
+        assert ei.value.code == ecf.ECF_EINVAL
