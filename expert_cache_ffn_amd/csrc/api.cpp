@@ -149,7 +149,8 @@ bool blob_layout(const ecf_shape &s, BlobLayout *out)
 int max_tiles(const ecf_shape &s, int32_t T)
 {
     const int R = T * s.top_k;
-    return (R + kPrefillMT - 1) / kPrefillMT + std::min(s.n_experts, R);
+    const int mt = prefill_mt(s);
+    return (R + mt - 1) / mt + std::min(s.n_experts, R);
 }
 
 WsLayout ws_layout(const ecf_shape &s, int32_t T)

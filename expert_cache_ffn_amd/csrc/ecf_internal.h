@@ -49,7 +49,10 @@ struct ProfScope {
 // ---- geometry ------------------------------------------------------------------
 constexpr int kSortSeg = 1024;      // rows per segment of the multi-block counting sort
 constexpr int kSmallRouteRows = 2048; // R up to this uses the single-block routing kernel
-constexpr int kPrefillMT = 128;     // rows per prefill GEMM tile
+constexpr int kPrefillMT = 128;     // rows per prefill GEMM tile (bf16 weights)
+#ifndef ECF_MX_BM
+#define ECF_MX_BM 128                // rows per prefill GEMM tile (MXFP4 weights)
+#endif
 constexpr int kDecodeNT = 2;        // max rows per pass of the decode GEMV kernels
 
 struct BlobLayout {
@@ -65,6 +68,8 @@ struct WsLayout {
 };
 WsLayout ws_layout(const ecf_shape &s, int32_t T);
 int max_tiles(const ecf_shape &s, int32_t T);
+// Rows per prefill GEMM tile for this shape; the routing kernels build the tile list with it.
+inline int prefill_mt(const ecf_shape &s) { return s.w_dtype == ECF_MXFP4 ? ECF_MX_BM : kPrefillMT; }
 
 // ---- kernel launchers (k_*.hip) -------------------------------------------------
 struct RouteOut {

@@ -37,8 +37,7 @@
 namespace ecf {
 
 namespace {
-constexpr int BM = kPrefillMT;  // 128 rows per tile
-constexpr int BK = 64;          // reduction elements per stage
+constexpr int BK = 64;  // reduction elements per stage
 
 // bf16 tile rows of eight 16-B chunks; chunk c of row r sits at c ^ (r & 7) ^ bit 3
 // of r.  A 16-B-per-lane read of one chunk over rows r0..r0+15 then touches 16
@@ -92,31 +91,32 @@ __device__ __forceinline__ bf16x8_t cvt_mx8(uint32_t w, float s)
 // One stage of global data held in registers between load and LDS store.
 // BNT = weight rows per block tile; NBL = 16-B B chunks per thread and stage.
 // A stage covers KS sub-tiles of BK = 64 reduction elements each.
-template <bool MX, int BNT, int KS>
+template <bool MX, int BM, int BNT, int KS>
 struct Stage {
+    static constexpr int NAL = BM / 32;  // 16-B A chunks per thread and sub-tile
     static constexpr int NBL = MX ? BNT / 128 : BNT / 32;
-    u32x4_t a[4 * KS];        // A: rows (tid>>3) + 32q, chunk tid&7, per sub-tile
+    u32x4_t a[NAL * KS];      // A: rows (tid>>3) + 32q, chunk tid&7, per sub-tile
     u32x4_t b[NBL * KS];      // B bf16: rows (tid>>3) + 32q; MX: rows (tid>>1) + 128q, half tid&1
     uint32_t s;               // MX: the 2*KS scale bytes of row tid (tid < BNT)
 };
 
-template <bool MX, int BNT>
+template <bool MX, int BM, int BNT>
 struct Ptrs {
-    const char *a[4];
+    const char *a[BM / 32];
     const char *b[MX ? BNT / 128 : BNT / 32];
     const uint8_t *s;
 };
 
-template <bool MX, int BNT, int KS>
-__device__ __forceinline__ void gload(Stage<MX, BNT, KS> &st, const Ptrs<MX, BNT> &p, int kt, int tid)
+template <bool MX, int BM, int BNT, int KS>
+__device__ __forceinline__ void gload(Stage<MX, BM, BNT, KS> &st, const Ptrs<MX, BM, BNT> &p, int kt, int tid)
 {
-    constexpr int NBL = Stage<MX, BNT, KS>::NBL;
+    constexpr int NAL = Stage<MX, BM, BNT, KS>::NAL, NBL = Stage<MX, BM, BNT, KS>::NBL;
 #pragma unroll
     for (int sub = 0; sub < KS; ++sub) {
         const size_t col = (size_t)(kt * KS + sub) * BK;  // first reduction element of the sub-tile
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            st.a[sub * 4 + q] = ldg16(p.a[q] + col * 2);
+        for (int q = 0; q < NAL; ++q)
+            st.a[sub * NAL + q] = ldg16(p.a[q] + col * 2);
 #pragma unroll
         for (int q = 0; q < NBL; ++q)
             st.b[sub * NBL + q] = ldg16(p.b[q] + (MX ? col / 2 : col * 2));
@@ -132,16 +132,17 @@ __device__ __forceinline__ void gload(Stage<MX, BNT, KS> &st, const Ptrs<MX, BNT
 // Bs + sub * (B tile size).  MX scales are widened to fp32 here, once per row
 // and stage, and stored group-major: Scf[group * (BNT + 32) + row] (the pad
 // puts the two lane halves' reads on different banks).
-template <bool MX, int BNT, int KS>
-__device__ __forceinline__ void sstore(const Stage<MX, BNT, KS> &st, u32x4_t *As, u32x4_t *Bs, float *Scf, int tid)
+template <bool MX, int BM, int BNT, int KS>
+__device__ __forceinline__ void sstore(const Stage<MX, BM, BNT, KS> &st, u32x4_t *As, u32x4_t *Bs, float *Scf,
+                                       int tid)
 {
-    constexpr int NBL = Stage<MX, BNT, KS>::NBL;
+    constexpr int NAL = Stage<MX, BM, BNT, KS>::NAL, NBL = Stage<MX, BM, BNT, KS>::NBL;
     constexpr int BT = MX ? BNT * 2 : BNT * 8;  // 16-B slots of one B sub-tile
 #pragma unroll
     for (int sub = 0; sub < KS; ++sub) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            As[sub * BM * 8 + swz((tid >> 3) + 32 * q, tid & 7)] = st.a[sub * 4 + q];
+        for (int q = 0; q < NAL; ++q)
+            As[sub * BM * 8 + swz((tid >> 3) + 32 * q, tid & 7)] = st.a[sub * NAL + q];
 #pragma unroll
         for (int q = 0; q < NBL; ++q) {
             if (MX)
@@ -184,7 +185,7 @@ struct IC {
 // and B alike, so every chunk is used once.  Lane half g then reads the 32
 // MXFP4 elements 32g..32g+31 -- 16 bytes, exactly one E8M0 scale group -- with
 // a single LDS read per k-tile.
-template <int MODE, bool MX, int BNT, int MINB, int KS, int WM>
+template <int MODE, bool MX, int BM, int BNT, int MINB, int KS, int WM>
 __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
     const uint64_t *__restrict__ ptrs, size_t off_w0, size_t off_w1, size_t off_s0, size_t off_s1,
     const int32_t *__restrict__ tiles, const int32_t *__restrict__ n_tiles,
@@ -216,9 +217,9 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
     // MODE 1: this block's intermediate columns [n0, n0 + BNT/2); MODE 2: outputs [n0, n0 + BNT)
     const int n0 = nt * (MODE == 1 ? BNT / 2 : BNT);
 
-    Ptrs<MX, BNT> p;
+    Ptrs<MX, BM, BNT> p;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < BM / 32; ++q) {
         const int row = min((tid >> 3) + 32 * q, mrows - 1);
         const size_t arow = MODE == 1 ? (size_t)(perm[rb + row] / k) : (size_t)(rb + row);
         p.a[q] = (const char *)(A + arow * lda + (tid & 7) * 8);
@@ -274,10 +275,10 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
 #pragma unroll
                 for (int j = 0; j < 16; ++j)
                     acc[a][b][j] = 0.f;
-        Stage<MX, BNT, KS> s0, s1;
-        gload<MX, BNT, KS>(s0, p, 0, tid);
-        gload<MX, BNT, KS>(s1, p, 1, tid);
-        sstore<MX, BNT, KS>(s0, As[0], Bs[0], Scf[0], tid);
+        Stage<MX, BM, BNT, KS> s0, s1;
+        gload<MX, BM, BNT, KS>(s0, p, 0, tid);
+        gload<MX, BM, BNT, KS>(s1, p, 1, tid);
+        sstore<MX, BM, BNT, KS>(s0, As[0], Bs[0], Scf[0], tid);
         __syncthreads();
         // NXT holds k-tile kt+1 (loaded one iteration ago); FRE is free and
         // receives k-tile kt+2.  Two copies of the body alternate the roles so
@@ -289,7 +290,7 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
 #define ECF_GEMM_BODY(KT, NXT, FRE)                                                                  \
     {                                                                                               \
         const int cur = (KT) & 1;                                                                   \
-        gload<MX, BNT, KS>(FRE, p, min((KT) + 2, nk - 1), tid);                                     \
+        gload<MX, BM, BNT, KS>(FRE, p, min((KT) + 2, nk - 1), tid);                                 \
         if (NMS > 0) {                                                                              \
             _Pragma("unroll") for (int sub = 0; sub < KS; ++sub)                                    \
             {                                                                                       \
@@ -315,7 +316,7 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
                 }                                                                                   \
             }                                                                                       \
         }                                                                                           \
-        sstore<MX, BNT, KS>(NXT, As[cur ^ 1], Bs[cur ^ 1], Scf[cur ^ 1], tid);                      \
+        sstore<MX, BM, BNT, KS>(NXT, As[cur ^ 1], Bs[cur ^ 1], Scf[cur ^ 1], tid);                  \
         __syncthreads();                                                                            \
     }
         for (int kt = 0; kt < nk; kt += 2) {
@@ -348,21 +349,27 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
     // MFMA row blocks of this wave that hold real rows (uniform over the wave)
     // (with WM = 1 a block of 65..96 rows runs 4 row blocks: one wasted, one fewer instance)
     const int nms = __builtin_amdgcn_readfirstlane(max(0, min(NMSMAX, (mrows - wm * WROWS + 31) / 32)));
-    if (WM == 1) {
-        if (nms > 2)
+    if constexpr (NMSMAX >= 4) {
+        if (nms >= 4) {
             run(IC<NMSMAX>{});
-        else if (nms == 2)
-            run(IC<2>{});
-        else
-            run(IC<1>{});
-    } else {
-        if (nms == 2)
-            run(IC<2>{});
-        else if (nms == 1)
-            run(IC<1>{});
-        else
-            run(IC<0>{});
+            return;
+        }
+        if (nms == 3) {
+            run(IC<3>{});
+            return;
+        }
+    } else if constexpr (NMSMAX == 3) {
+        if (nms == 3) {
+            run(IC<3>{});
+            return;
+        }
     }
+    if (nms == 2)
+        run(IC<2>{});
+    else if (nms == 1)
+        run(IC<1>{});
+    else
+        run(IC<0>{});
 }
 
 // ---------------------------------------------------------------------------------
@@ -396,7 +403,7 @@ int launch_prefill_gemm1(const ecf_shape &s, const ExpertTables &ex, const Route
     const int nblk = max_tiles(s, T) * NT;
     ProfScope p("prefill_gemm1", st);
 #define ECF_G1(MXV, BNV, MBV, KSV, WMV)                                                                    \
-    hipLaunchKernelGGL((k_grouped_gemm<1, MXV, BNV, MBV, KSV, WMV>), dim3(nblk), dim3(256), 0, st, ex.ptrs,  \
+    hipLaunchKernelGGL((k_grouped_gemm<1, MXV, (MXV) ? ECF_MX_BM : kPrefillMT, BNV, MBV, KSV, WMV>), dim3(nblk), dim3(256), 0, st, ex.ptrs,  \
                        ex.lay.off[0], ex.lay.off[1], ex.lay.off[3], ex.lay.off[4], o.tiles, o.n_tiles,         \
                        o.offsets, o.perm, (const uint16_t *)x, s.hidden, s.inter, s.hidden, s.top_k,         \
                        s.n_experts, T * s.top_k, NT, (void *)H)
@@ -420,7 +427,7 @@ int launch_prefill_gemm2(const ecf_shape &s, const ExpertTables &ex, const Route
     const int nblk = max_tiles(s, T) * NT;
     ProfScope p("prefill_gemm2", st);
 #define ECF_G2(MXV, BNV, MBV, KSV, WMV)                                                                    \
-    hipLaunchKernelGGL((k_grouped_gemm<2, MXV, BNV, MBV, KSV, WMV>), dim3(nblk), dim3(256), 0, st, ex.ptrs,  \
+    hipLaunchKernelGGL((k_grouped_gemm<2, MXV, (MXV) ? ECF_MX_BM : kPrefillMT, BNV, MBV, KSV, WMV>), dim3(nblk), dim3(256), 0, st, ex.ptrs,  \
                        ex.lay.off[2], ex.lay.off[2], ex.lay.off[5], ex.lay.off[5], o.tiles, o.n_tiles,         \
                        o.offsets, o.perm, H, s.inter, s.hidden, s.inter, s.top_k, s.n_experts, T * s.top_k,  \
                        NT, (void *)Y)

@@ -448,7 +448,7 @@ int launch_route(const ecf_shape &s, const float *logits, int T, const RouteOut 
         const size_t sh = sizeof(int) * (size_t)(R + E);
 #define ECF_ROUTE_SMALL(MS)                                                                       \
     hipLaunchKernelGGL((k_route_small<MS>), dim3(1), dim3(1024), sh, st, logits, T, E, k,         \
-                       s.renorm_topk, kPrefillMT, o.idx, o.gate, o.counts, o.offsets, o.perm,      \
+                       s.renorm_topk, prefill_mt(s), o.idx, o.gate, o.counts, o.offsets, o.perm,      \
                        o.pos, o.active, o.n_active, o.tiles, o.n_tiles)
         if (maxs <= 1)
             ECF_ROUTE_SMALL(1);
@@ -492,7 +492,7 @@ int launch_route(const ecf_shape &s, const float *logits, int T, const RouteOut 
     }
     {
         ProfScope p("sort_scan", st);
-        hipLaunchKernelGGL(k_sort_scan, dim3(1), dim3(1024), 0, st, o.seg_counts, S, E, kPrefillMT,
+        hipLaunchKernelGGL(k_sort_scan, dim3(1), dim3(1024), 0, st, o.seg_counts, S, E, prefill_mt(s),
                            o.seg_base, o.counts, o.offsets, o.active, o.n_active, o.tiles,
                            o.n_tiles);
         ECF_HIP_CHECK(hipGetLastError());
