@@ -191,7 +191,7 @@ def bench_decode(torch, ecf, syn, Ts, steps, warmup, n_batches=64, use_graph=Tru
     return results, sample
 
 
-def cpu_baseline_decode(torch, syn, sample, budget_s=12.0, T=16):
+def cpu_baseline_decode(torch, syn, sample, budget_s=15.0, T=16, max_batches=256):
     """The oracle (C, OpenMP over tokens) on whole T=16 batches until ~budget_s."""
     import numpy as np
     import oracle
@@ -215,7 +215,7 @@ def cpu_baseline_decode(torch, syn, sample, budget_s=12.0, T=16):
         return cache[e]
 
     done, elapsed, batches = 0, 0.0, 0
-    while elapsed < budget_s and batches < 64:
+    while elapsed < budget_s and batches < max_batches:
         x = syn.activations(cfg, T, batch=batches)
         lg = oracle.logits(x, wr)
         idx, g = oracle.route(lg, cfg.top_k)
