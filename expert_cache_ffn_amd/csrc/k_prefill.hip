@@ -16,16 +16,20 @@
 // Block = 4 waves (2 x 2), tile 128 rows x BNT weight rows (BNT = 128 for bf16,
 // 256 for MXFP4), BK = 64; each wave owns 64 rows x BNT/2 weight rows (2 x
 // BNT/64 MFMA 32x32 fragments).  Software pipeline of depth 2 through
-// registers: the global loads of k-tile kt+2 are issued before the MFMAs of
-// k-tile kt, and stored to the free LDS buffer after them, so over a k-tile of
-// MFMA work covers each load's latency.  (Direct global->LDS loads were measured against: the compiler
-// cannot tell which in-flight LDS DMA a later LDS read depends on and drains
-// them all, which serialises the pipeline.)
+// registers: in program order the loads of k-tile kt+2 come before the MFMAs
+// of k-tile kt and the LDS stores of k-tile kt+1 after them (the compiler's
+// schedule of that order measured faster than pinning it with scheduling
+// barriers).  Operands arrive by raw buffer loads: one 32-bit offset register
+// per row, the k-tile's column in a scalar offset.  (Direct global->LDS loads
+// were measured against: the compiler cannot tell which in-flight LDS DMA a
+// later LDS read depends on and drains them all, which serialises the
+// pipeline.)
 //
 // bf16 rows of 64 elements (eight 16-B chunks) sit in LDS XOR-swizzled (see
-// swz), so the 32 rows one MFMA operand read touches spread over the banks.  MXFP4 weights stay 4-bit in LDS (a quarter of the bf16 bytes) and
-// are expanded in registers by v_cvt_scalef32_pk_bf16_fp4, which applies the
-// E8M0 block scale exactly; products run on bf16 MFMA.
+// swz), so the 32 rows one MFMA operand read touches spread over the banks.
+// MXFP4 weights stay 4-bit in LDS (a quarter of the bf16 bytes) and are
+// expanded in registers by v_cvt_scalef32_pk_bf16_fp4, which applies the E8M0
+// block scale exactly; products run on bf16 MFMA.
 //
 // Blocks are issued round-robin over the 8 XCDs (block b runs on XCD b % 8),
 // each with its own L2.  The 1-D block index is remapped so each XCD walks a
@@ -58,17 +62,6 @@ __device__ __forceinline__ float e8m0_f(uint32_t s)
     return __uint_as_float(s == 0 ? 0x00400000u : s == 255 ? 0x7FC00000u : (s << 23));
 }
 
-// 16-byte load through a global-address-space pointer (the blob addresses come
-// from a device table, so they would otherwise be generic/flat pointers).
-typedef const __attribute__((address_space(1))) u32x4_t *gptr16;
-typedef const __attribute__((address_space(1))) uint16_t *gptr2;
-typedef const __attribute__((address_space(1))) uint32_t *gptr4;
-__device__ __forceinline__ u32x4_t ldg16(const void *p) { return *(gptr16)(uintptr_t)p; }
-__device__ __forceinline__ uint32_t ldg2(const void *p) { return *(gptr2)(uintptr_t)p; }
-__device__ __forceinline__ uint32_t ldg4(const void *p) { return *(gptr4)(uintptr_t)p; }
-typedef const __attribute__((address_space(1))) uint8_t *gptr1;
-__device__ __forceinline__ uint32_t ldg1(const void *p) { return *(gptr1)(uintptr_t)p; }
-
 __device__ __forceinline__ bf16x8_t frag_bf16(const u32x4_t *tile, int row, int kc)
 {
     return __builtin_bit_cast(bf16x8_t, tile[swz(row, kc)]);
@@ -100,32 +93,46 @@ struct Stage {
     uint32_t s;               // MX: the 2*KS scale bytes of row tid (tid < BNT)
 };
 
+// Operand loads are raw buffer loads: a block-uniform resource (base and byte
+// size, in scalar registers), this thread's 32-bit row offset, and the k-tile's
+// column offset as the uniform soffset -- one VGPR per row and no per-k-tile
+// address arithmetic in vector registers.  A load at or past the size returns 0.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    // 0x00020000: word 3 of a raw-buffer resource on gfx9 parts (32-bit data format)
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+
 template <bool MX, int BM, int BNT>
 struct Ptrs {
-    const char *a[BM / 32];
-    const char *b[MX ? BNT / 128 : BNT / 32];
-    const uint8_t *s;
+    uint32_t a[BM / 32];                    // A rows, this thread's 16-B chunk (bytes from A's base)
+    uint32_t b[MX ? BNT / 128 : BNT / 32];  // B rows within the blob, this thread's 16-B chunk
+    uint32_t s;                             // MX: this thread's scale row within the blob
 };
 
 template <bool MX, int BM, int BNT, int KS>
-__device__ __forceinline__ void gload(Stage<MX, BM, BNT, KS> &st, const Ptrs<MX, BM, BNT> &p, int kt, int tid)
+__device__ __forceinline__ void gload(Stage<MX, BM, BNT, KS> &st, const Ptrs<MX, BM, BNT> &p, rsrc_t ra, rsrc_t rb,
+                                      int kt, int tid)
 {
     constexpr int NAL = Stage<MX, BM, BNT, KS>::NAL, NBL = Stage<MX, BM, BNT, KS>::NBL;
 #pragma unroll
     for (int sub = 0; sub < KS; ++sub) {
-        const size_t col = (size_t)(kt * KS + sub) * BK;  // first reduction element of the sub-tile
+        const int col = (kt * KS + sub) * BK;  // first reduction element of the sub-tile
 #pragma unroll
         for (int q = 0; q < NAL; ++q)
-            st.a[sub * NAL + q] = ldg16(p.a[q] + col * 2);
+            st.a[sub * NAL + q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, p.a[q], col * 2, 0));
 #pragma unroll
         for (int q = 0; q < NBL; ++q)
-            st.b[sub * NBL + q] = ldg16(p.b[q] + (MX ? col / 2 : col * 2));
+            st.b[sub * NBL + q] = __builtin_bit_cast(
+                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rb, p.b[q], MX ? col / 2 : col * 2, 0));
     }
     // every thread loads (threads past BNT re-read row 0's scales), so the number
     // of loads in flight is the same on every path and the compiler's load
     // counters can wait for exactly the older stage
     if (MX)
-        st.s = KS == 2 ? ldg4(p.s + (size_t)kt * 4) : ldg2(p.s + (size_t)kt * 2);
+        st.s = KS == 2 ? __builtin_amdgcn_raw_buffer_load_b32(rb, p.s, kt * 4, 0)
+                       : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, p.s, kt * 2, 0);
 }
 
 // Registers -> LDS.  Sub-tile `sub` of A sits at As + sub * BM * 8 and of B at
@@ -152,9 +159,14 @@ __device__ __forceinline__ void sstore(const Stage<MX, BM, BNT, KS> &st, u32x4_t
         }
     }
     if (MX && (BNT >= 256 || tid < BNT)) {
+        // The empty asm keeps the widening here, after the stage's other stores:
+        // left free, the compiler hoists it next to the load, and waiting for
+        // that load there waits for every load issued before it.
+        uint32_t sc = st.s;
+        asm volatile("" : "+v"(sc));
 #pragma unroll
         for (int gi = 0; gi < 2 * KS; ++gi)
-            Scf[gi * (BNT + 32) + tid] = e8m0_f((st.s >> (8 * gi)) & 0xffu);
+            Scf[gi * (BNT + 32) + tid] = e8m0_f((sc >> (8 * gi)) & 0xffu);
     }
 }
 
@@ -190,7 +202,7 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
     const uint64_t *__restrict__ ptrs, size_t off_w0, size_t off_w1, size_t off_s0, size_t off_s1,
     const int32_t *__restrict__ tiles, const int32_t *__restrict__ n_tiles,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm, const uint16_t *__restrict__ A,
-    int K, int N, int lda, int k, int E, int R, int NT, void *__restrict__ out)
+    int K, int N, int lda, int k, int E, int R, int NT, uint32_t blob_bytes, void *__restrict__ out)
 {
     constexpr int NCB = BNT / 64;  // 32-column MFMA blocks per wave
     constexpr int BT = MX ? BNT * 2 : BNT * 8;  // 16-B slots of one B sub-tile
@@ -221,9 +233,14 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
 #pragma unroll
     for (int q = 0; q < BM / 32; ++q) {
         const int row = min((tid >> 3) + 32 * q, mrows - 1);
-        const size_t arow = MODE == 1 ? (size_t)(perm[rb + row] / k) : (size_t)(rb + row);
-        p.a[q] = (const char *)(A + arow * lda + (tid & 7) * 8);
+        const size_t arow = MODE == 1 ? (size_t)(perm[rb + row] / k) : (size_t)row;  // from abase
+        p.a[q] = (uint32_t)(arow * lda * 2 + (tid & 7) * 16);
     }
+    // A: all of x (MODE 1; under 4 GiB, checked by the launcher) or the rows from
+    // the tile's first on (MODE 2); B: the blob
+    const size_t abytes = MODE == 1 ? (size_t)(R / k) * lda * 2 : (size_t)(R - rb) * lda * 2;
+    const rsrc_t ra = make_rsrc(A + (MODE == 1 ? 0 : (size_t)rb * lda), (uint32_t)min(abytes, (size_t)0xFFFFFFFFu));
+    const rsrc_t rbs = make_rsrc((const void *)blob, blob_bytes);
     // weight row r of the block's B tile -> (section, scale section, matrix row)
     auto brow = [&](int r, size_t &sec_off, size_t &sc_off) {
         if (MODE == 1) {
@@ -240,19 +257,19 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
         for (int q = 0; q < (MX ? BNT / 128 : BNT / 32); ++q) {
             size_t so, sco;
             const int r = brow((tid >> 1) + 128 * q, so, sco);
-            p.b[q] = (const char *)blob + so + (size_t)r * (K / 2) + (tid & 1) * 16;
+            p.b[q] = (uint32_t)(so + (size_t)r * (K / 2) + (tid & 1) * 16);
         }
         size_t so, sco;
         const int r = brow(tid < BNT ? tid : 0, so, sco);
-        p.s = (const uint8_t *)blob + sco + (size_t)r * (K / 32);
+        p.s = (uint32_t)(sco + (size_t)r * (K / 32));
     } else {
 #pragma unroll
         for (int q = 0; q < (MX ? BNT / 128 : BNT / 32); ++q) {
             size_t so, sco;
             const int r = brow((tid >> 3) + 32 * q, so, sco);
-            p.b[q] = (const char *)blob + so + (size_t)r * K * 2 + (tid & 7) * 16;
+            p.b[q] = (uint32_t)(so + (size_t)r * K * 2 + (tid & 7) * 16);
         }
-        p.s = nullptr;
+        p.s = 0;
     }
     // B-tile rows (lane's row within each of this wave's column blocks)
     int brw[NCB];
@@ -276,8 +293,8 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
                 for (int j = 0; j < 16; ++j)
                     acc[a][b][j] = 0.f;
         Stage<MX, BM, BNT, KS> s0, s1;
-        gload<MX, BM, BNT, KS>(s0, p, 0, tid);
-        gload<MX, BM, BNT, KS>(s1, p, 1, tid);
+        gload<MX, BM, BNT, KS>(s0, p, ra, rbs, 0, tid);
+        gload<MX, BM, BNT, KS>(s1, p, ra, rbs, 1, tid);
         sstore<MX, BM, BNT, KS>(s0, As[0], Bs[0], Scf[0], tid);
         __syncthreads();
         // NXT holds k-tile kt+1 (loaded one iteration ago); FRE is free and
@@ -290,7 +307,7 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
 #define ECF_GEMM_BODY(KT, NXT, FRE)                                                                  \
     {                                                                                               \
         const int cur = (KT) & 1;                                                                   \
-        gload<MX, BM, BNT, KS>(FRE, p, min((KT) + 2, nk - 1), tid);                                 \
+        gload<MX, BM, BNT, KS>(FRE, p, ra, rbs, min((KT) + 2, nk - 1), tid);                        \
         if (NMS > 0) {                                                                              \
             _Pragma("unroll") for (int sub = 0; sub < KS; ++sub)                                    \
             {                                                                                       \
@@ -400,13 +417,17 @@ int launch_prefill_gemm1(const ecf_shape &s, const ExpertTables &ex, const Route
     const bool mx = s.w_dtype == ECF_MXFP4;
     const int bnt = mx ? ECF_MX_BNT : ECF_BF16_BNT;
     const int NT = s.inter / (bnt / 2);
+    // the kernel addresses x rows and blob rows with 32-bit byte offsets
+    if ((size_t)T * s.hidden * 2 > 0xFFFFFFFFull || ex.lay.bytes > 0xFFFFFFFFull)
+        return set_error(ECF_EUNSUPPORTED, "prefill path: x (%d x %d bf16) and one expert blob (%zu B) must each "
+                         "be under 4 GiB", T, s.hidden, ex.lay.bytes);
     const int nblk = max_tiles(s, T) * NT;
     ProfScope p("prefill_gemm1", st);
 #define ECF_G1(MXV, BNV, MBV, KSV, WMV)                                                                    \
     hipLaunchKernelGGL((k_grouped_gemm<1, MXV, (MXV) ? ECF_MX_BM : kPrefillMT, BNV, MBV, KSV, WMV>), dim3(nblk), dim3(256), 0, st, ex.ptrs,  \
                        ex.lay.off[0], ex.lay.off[1], ex.lay.off[3], ex.lay.off[4], o.tiles, o.n_tiles,         \
                        o.offsets, o.perm, (const uint16_t *)x, s.hidden, s.inter, s.hidden, s.top_k,         \
-                       s.n_experts, T * s.top_k, NT, (void *)H)
+                       s.n_experts, T * s.top_k, NT, (uint32_t)ex.lay.bytes, (void *)H)
     // K = d; the main loop takes an even number of stages of KS sub-tiles: d % (128 * KS) == 0
     // (d is a multiple of 256)
     if (mx)
@@ -424,13 +445,15 @@ int launch_prefill_gemm2(const ecf_shape &s, const ExpertTables &ex, const Route
     const bool mx = s.w_dtype == ECF_MXFP4;
     const int bnt = mx ? ECF_MX_BNT : ECF_BF16_BNT;
     const int NT = s.hidden / bnt;
+    if (ex.lay.bytes > 0xFFFFFFFFull)  // blob rows are addressed with 32-bit byte offsets
+        return set_error(ECF_EUNSUPPORTED, "prefill path: one expert blob (%zu B) must be under 4 GiB", ex.lay.bytes);
     const int nblk = max_tiles(s, T) * NT;
     ProfScope p("prefill_gemm2", st);
 #define ECF_G2(MXV, BNV, MBV, KSV, WMV)                                                                    \
     hipLaunchKernelGGL((k_grouped_gemm<2, MXV, (MXV) ? ECF_MX_BM : kPrefillMT, BNV, MBV, KSV, WMV>), dim3(nblk), dim3(256), 0, st, ex.ptrs,  \
                        ex.lay.off[2], ex.lay.off[2], ex.lay.off[5], ex.lay.off[5], o.tiles, o.n_tiles,         \
                        o.offsets, o.perm, H, s.inter, s.hidden, s.inter, s.top_k, s.n_experts, T * s.top_k,  \
-                       NT, (void *)Y)
+                       NT, (uint32_t)ex.lay.bytes, (void *)Y)
     // K = I; the main loop takes an even number of stages: two-sub-tile stages
     // only when I % 256 == 0 (I % 128 == 0 holds on this path)
     if (mx) {

@@ -207,7 +207,8 @@ typedef struct {
                                     I % 128 != 0; the prefill grouped GEMM otherwise (bf16 /
                                     MXFP4, all-resident only: it rounds h to bf16, the host
                                     experts do not, so cache mode + PREFILL is
-                                    ECF_EUNSUPPORTED) */
+                                    ECF_EUNSUPPORTED; it also needs x and one expert
+                                    blob each under 4 GiB, else ECF_EUNSUPPORTED) */
     /* buffers */
     void *d_ws;                  /* workspace, >= ecf_workspace_bytes(shape, T) bytes, 256-B aligned */
     size_t ws_bytes;
