@@ -350,41 +350,69 @@ __global__ __launch_bounds__(256) void k_sort_count(const int32_t *__restrict__ 
         seg_counts[(size_t)blockIdx.x * E + e] = hist[e];
 }
 
+// One block.  Expert e's segments are split over P = min(16, 1024 / E) threads
+// (thread t: expert t % E, part t / E, a contiguous run of segments each), so
+// the per-segment loads are spread out and batched instead of walked by one
+// thread; the parts' sums meet in LDS, then each part writes its bases.
 __global__ __launch_bounds__(1024) void k_sort_scan(
     const int32_t *__restrict__ seg_counts, int S, int E, int MT, int32_t *__restrict__ seg_base,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ active,
     int32_t *__restrict__ n_active, int32_t *__restrict__ tiles, int32_t *__restrict__ n_tiles)
 {
     __shared__ int sc[17];
-    const int e = threadIdx.x;
+    __shared__ int part[1024];  // part[p * E + e]: rows of expert e in part p's segments
+    __shared__ int eoff[1024];  // first sorted row of expert e
+    const int P = min(16, max(1, 1024 / E));
+    const int t = threadIdx.x, e = t % E, p = t / E;
+    const bool on = p < P;
+    const int s0 = on ? (int)((int64_t)S * p / P) : 0, s1 = on ? (int)((int64_t)S * (p + 1) / P) : 0;
     int c = 0;
-    if (e < E)
-        for (int s = 0; s < S; ++s) {
-            const int v = seg_counts[(size_t)s * E + e];
-            seg_base[(size_t)s * E + e] = c;
-            c += v;
+#pragma unroll 8
+    for (int s = s0; s < s1; ++s)
+        c += seg_counts[(size_t)s * E + e];
+    if (on)
+        part[t] = c;
+    __syncthreads();
+    int pre = 0, ce = 0;  // rows of e in parts before p; all rows of e
+    if (on)
+        for (int q = 0; q < P; ++q) {
+            const int v = part[q * E + e];
+            pre += q < p ? v : 0;
+            ce += v;
         }
+    // the expert-level scans run over the part-0 threads, which are threads 0..E-1
+    const bool lead = on && p == 0;
+    const int cl = lead ? ce : 0;
     int tot, na, ntt;
-    const int off = block_excl_scan(c, sc, &tot);
-    const int aoff = block_excl_scan(c > 0 ? 1 : 0, sc, &na);
-    const int nte = (c + MT - 1) / MT;
+    const int off = block_excl_scan(cl, sc, &tot);
+    const int aoff = block_excl_scan(cl > 0 ? 1 : 0, sc, &na);
+    const int nte = (cl + MT - 1) / MT;
     const int toff = block_excl_scan(nte, sc, &ntt);
-    if (e < E) {
-        counts[e] = c;
+    if (lead) {
+        counts[e] = cl;
         offsets[e] = off;
-        for (int s = 0; s < S; ++s)
-            seg_base[(size_t)s * E + e] += off;
-        if (c > 0)
+        eoff[e] = off;
+        if (cl > 0)
             active[aoff] = e;
         for (int m = 0; m < nte; ++m) {
             tiles[2 * (toff + m)] = e;
             tiles[2 * (toff + m) + 1] = m * MT;
         }
     }
-    if (e == 0) {
+    if (t == 0) {
         offsets[E] = tot;
         *n_active = na;
         *n_tiles = ntt;
+    }
+    __syncthreads();
+    if (on) {
+        int run = eoff[e] + pre;
+#pragma unroll 8
+        for (int s = s0; s < s1; ++s) {
+            const int v = seg_counts[(size_t)s * E + e];
+            seg_base[(size_t)s * E + e] = run;
+            run += v;
+        }
     }
 }
 

@@ -117,7 +117,10 @@ def test_residual_added():
 
 # ---- prefill bf16 (grouped MFMA GEMM) ---------------------------------------------------
 
-@pytest.mark.parametrize("T,E,k,I", [(300, 8, 2, 256), (1000, 4, 2, 128), (97, 32, 6, 384), (700, 3, 1, 256)])
+# T*k above 2048 takes the multi-block counting sort: 1500 x 2 over 4 experts and
+# 2100 x 1 over 3 (16 scan parts per expert, some with no segments), 600 x 4 over 16
+@pytest.mark.parametrize("T,E,k,I", [(300, 8, 2, 256), (1000, 4, 2, 128), (97, 32, 6, 384), (700, 3, 1, 256),
+                                     (1500, 4, 2, 128), (2100, 3, 1, 128), (600, 16, 4, 128)])
 def test_prefill_bf16_ragged_tiles(T, E, k, I):
     cfg = cfg_small(experts=E, top_k=k, inter=I, logits="uniform", cid=70 + E)
     say(f"case: prefill bf16 T={T} E={E} k={k} I={I}")
