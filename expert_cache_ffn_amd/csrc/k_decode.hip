@@ -400,17 +400,29 @@ __global__ __launch_bounds__(256) void k_combine(
     const uint64_t *__restrict__ ptrs, const float *__restrict__ Y, int k, int d,
     int E, int R, const float *residual, const float *__restrict__ host_part, float *out, void *out_act)
 {
+    // The token's k (row, gate) pairs are read once into LDS (-1: expert not
+    // evaluated here), so the k row loads below do not wait on each other.
+    __shared__ int srow[32];
+    __shared__ float sg[32];
     const int t = blockIdx.y;
+    if ((int)threadIdx.x < k) {
+        const int f = t * k + threadIdx.x;
+        const int e = idx[f], p = pos[f];
+        const bool ok = (unsigned)e < (unsigned)E && (unsigned)p < (unsigned)R && ptrs[e];
+        srow[threadIdx.x] = ok ? p : -1;
+        sg[threadIdx.x] = gate[f];
+    }
+    __syncthreads();
     const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (c >= d)
         return;
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
     for (int j = 0; j < k; ++j) {
-        const int f = t * k + j;
-        const int e = idx[f], p = pos[f];
-        if ((unsigned)e >= (unsigned)E || (unsigned)p >= (unsigned)R || !ptrs[e])
+        const int p = srow[j];
+        if (p < 0)
             continue;
-        const float g = gate[f];
+        const float g = sg[j];
         const float4 y = *reinterpret_cast<const float4 *>(Y + (size_t)p * d + c);
         s.x = fmaf(g, y.x, s.x);
         s.y = fmaf(g, y.y, s.y);

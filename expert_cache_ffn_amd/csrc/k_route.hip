@@ -20,6 +20,74 @@
 namespace ecf {
 
 // ---------------------------------------------------------------------------------
+// Wave-wide reductions without LDS round trips: four DPP steps inside each row of
+// 16 lanes (xor 1, xor 2, mirror within 8, mirror within 16: afterwards every lane
+// of a row holds the same row result, each pair having combined the same two
+// operands), then the four row results read into scalar registers and combined in
+// row order.  The result is wave-uniform.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t x)
+{
+    return ((uint64_t)dpp32<CTRL>((uint32_t)(x >> 32)) << 32) | dpp32<CTRL>((uint32_t)x);
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x)
+{
+    x = umax64(x, dpp64<kDppXor1>(x));
+    x = umax64(x, dpp64<kDppXor2>(x));
+    x = umax64(x, dpp64<kDppHalfMirror>(x));
+    x = umax64(x, dpp64<kDppMirror>(x));
+    uint64_t r = 0;
+#pragma unroll
+    for (int row = 0; row < 4; ++row) {
+        const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 16 * row);
+        const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)x, 16 * row);
+        r = umax64(r, ((uint64_t)hi << 32) | lo);
+    }
+    return r;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float x)
+{
+    x += __uint_as_float(dpp32<kDppXor1>(__float_as_uint(x)));
+    x += __uint_as_float(dpp32<kDppXor2>(__float_as_uint(x)));
+    x += __uint_as_float(dpp32<kDppHalfMirror>(__float_as_uint(x)));
+    x += __uint_as_float(dpp32<kDppMirror>(__float_as_uint(x)));
+    const float r0 = __uint_as_float(__builtin_amdgcn_readlane((int)__float_as_uint(x), 0));
+    const float r1 = __uint_as_float(__builtin_amdgcn_readlane((int)__float_as_uint(x), 16));
+    const float r2 = __uint_as_float(__builtin_amdgcn_readlane((int)__float_as_uint(x), 32));
+    const float r3 = __uint_as_float(__builtin_amdgcn_readlane((int)__float_as_uint(x), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+__device__ __forceinline__ double wave_sum_f64(double x)
+{
+    const auto step = [](double v, uint64_t o) { return v + __longlong_as_double((long long)o); };
+    x = step(x, dpp64<kDppXor1>((uint64_t)__double_as_longlong(x)));
+    x = step(x, dpp64<kDppXor2>((uint64_t)__double_as_longlong(x)));
+    x = step(x, dpp64<kDppHalfMirror>((uint64_t)__double_as_longlong(x)));
+    x = step(x, dpp64<kDppMirror>((uint64_t)__double_as_longlong(x)));
+    double r[4];
+#pragma unroll
+    for (int row = 0; row < 4; ++row) {
+        const uint64_t b = (uint64_t)__double_as_longlong(x);
+        const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 16 * row);
+        const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)b, 16 * row);
+        r[row] = __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+    }
+    return (r[0] + r[1]) + (r[2] + r[3]);
+}
+
+// ---------------------------------------------------------------------------------
 // Router GEMV.  Block = one expert x TT tokens; its 4 waves interleave over d in
 // 16-byte vectors.  grid = (E, ceil(T / TT)).
 template <bool BF16, int TT>
@@ -73,7 +141,7 @@ __global__ __launch_bounds__(256) void k_router_logits(const void *__restrict__ 
     }
 #pragma unroll
     for (int q = 0; q < TT; ++q) {
-        double v = wave_sum(acc[q]);
+        const double v = wave_sum_f64(acc[q]);
         if (lane == 0)
             red[w][q] = v;
     }
@@ -85,65 +153,79 @@ __global__ __launch_bounds__(256) void k_router_logits(const void *__restrict__ 
     }
 }
 
+// Selection key of (logit v, expert e): the fp32 bits mapped to an unsigned
+// order-preserving code (sign folded), then the complement of e, so a larger
+// key is a larger logit, or an equal logit with a lower expert id.  -0 counts as
+// +0 (the two compare equal), NaN as -inf.  Key 0 = not selectable.
+__device__ __forceinline__ uint64_t sel_key(float v, int e)
+{
+    if (v != v)
+        v = -INFINITY;
+    uint32_t u = __float_as_uint(v == 0.f ? 0.f : v);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)e;
+}
+__device__ __forceinline__ float key_value(uint64_t key)
+{
+    const uint32_t u = (uint32_t)(key >> 32);
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
 // ---------------------------------------------------------------------------------
-// Top-k of one token's logits by one wave.  MAXS = logits held per lane.
+// Top-k of one token's logits by one wave.  MAXS = logits held per lane.  Each of
+// the k rounds takes the wave maximum of the lanes' best remaining keys; the
+// winner is wave-uniform and its owner lane retires it.
 template <int MAXS>
 __device__ __forceinline__ void topk_wave(const float *__restrict__ lg, int E, int k, int renorm,
                                           int lane, int32_t *idx_out, float *gate_out, int *sidx)
 {
-    float v[MAXS];
-    uint32_t taken = 0;
+    uint64_t key[MAXS];
 #pragma unroll
     for (int s = 0; s < MAXS; ++s) {
         const int e = lane + 64 * s;
-        float x = e < E ? lg[e] : -INFINITY;
-        if (x != x)
-            x = -INFINITY;
-        v[s] = x;
-        if (e >= E)
-            taken |= 1u << s;
+        key[s] = e < E ? sel_key(lg[e], e) : 0ull;
     }
-    float my_v = 0.f;
+    float my_v = 0.f, m0 = 0.f, rsum = 0.f;
     int my_e = 0;
     for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int be = INT_MAX;
+        uint64_t b = 0;
 #pragma unroll
-        for (int s = 0; s < MAXS; ++s) {
-            const int e = lane + 64 * s;
-            if (!((taken >> s) & 1u) && (v[s] > bv || (v[s] == bv && e < be))) {
-                bv = v[s];
-                be = e;
-            }
-        }
+        for (int s = 0; s < MAXS; ++s)
+            b = umax64(b, key[s]);
+        const uint64_t w = wave_max_u64(b);
+        const int we = (int)~(uint32_t)w;
+        const float wv = key_value(w);
+        if ((we & 63) == lane) {
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, 64);
-            const int oe = __shfl_xor(be, off, 64);
-            if (ov > bv || (ov == bv && oe < be)) {
-                bv = ov;
-                be = oe;
-            }
+            for (int s = 0; s < MAXS; ++s)
+                if (s == (we >> 6))
+                    key[s] = 0ull;
         }
-        if ((be & 63) == lane)
-            taken |= 1u << (be >> 6);
+        if (j == 0)
+            m0 = wv;
+        rsum += expf(wv - m0);  // the selected experts' softmax terms, j ascending
         if (lane == j) {
-            my_v = bv;
-            my_e = be;
+            my_v = wv;
+            my_e = we;
         }
     }
-    const float m0 = __shfl(my_v, 0, 64);
     const float ex = lane < k ? expf(my_v - m0) : 0.f;
     float denom;
     if (renorm) {
-        denom = wave_sum(ex);
+        denom = rsum;
     } else {
         float s = 0.f;
 #pragma unroll
-        for (int q = 0; q < MAXS; ++q)
-            if (lane + 64 * q < E)
-                s += expf(v[q] - m0);
-        denom = wave_sum(s);
+        for (int q = 0; q < MAXS; ++q) {
+            const int e = lane + 64 * q;
+            if (e < E) {
+                float v = lg[e];
+                if (v != v)
+                    v = -INFINITY;
+                s += expf(v - m0);
+            }
+        }
+        denom = wave_sum_f32(s);
     }
     if (lane < k) {
         idx_out[lane] = my_e;
@@ -170,27 +252,55 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
 
 // Exclusive scan of v over the block (blockDim multiple of 64, <= 1024).
 // sh: >= 17 ints of LDS.  *total receives the block sum.
+// Inclusive scan over the wave by DPP: row_shr 1, 2, 4, 8 inside each row of 16
+// lanes, then lane 15 of rows 0 and 2 into rows 1 and 3 (row_bcast:15), then
+// lane 31 into rows 2 and 3 (row_bcast:31).  Lanes a step does not write (no
+// source lane, or a row outside its row mask) take `old` = 0.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_or0(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWS, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x)
+{
+    x += dpp_or0<0x111, 0xF>(x);
+    x += dpp_or0<0x112, 0xF>(x);
+    x += dpp_or0<0x114, 0xF>(x);
+    x += dpp_or0<0x118, 0xF>(x);
+    x += dpp_or0<0x142, 0xA>(x);
+    x += dpp_or0<0x143, 0xC>(x);
+    return x;
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_or0_64(uint64_t x)
+{
+    return ((uint64_t)dpp_or0<CTRL, ROWS>((uint32_t)(x >> 32)) << 32) | dpp_or0<CTRL, ROWS>((uint32_t)x);
+}
+__device__ __forceinline__ uint64_t wave_incl_scan64(uint64_t x)
+{
+    x += dpp_or0_64<0x111, 0xF>(x);
+    x += dpp_or0_64<0x112, 0xF>(x);
+    x += dpp_or0_64<0x114, 0xF>(x);
+    x += dpp_or0_64<0x118, 0xF>(x);
+    x += dpp_or0_64<0x142, 0xA>(x);
+    x += dpp_or0_64<0x143, 0xC>(x);
+    return x;
+}
+
 __device__ int block_excl_scan(int v, int *sh, int *total)
 {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off, 64);
-        if (lane >= off)
-            x += y;
-    }
+    const int x = (int)wave_incl_scan((uint32_t)v);
     if (lane == 63)
         sh[w] = x;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int run = 0;
-        for (int i = 0; i < nw; ++i) {
-            const int t = sh[i];
-            sh[i] = run;
-            run += t;
-        }
-        sh[16] = run;
+    if (w == 0) {  // the (at most 16) wave totals, scanned by wave 0
+        const int t = lane < nw ? sh[lane] : 0;
+        const int inc = (int)wave_incl_scan((uint32_t)t);
+        if (lane < nw)
+            sh[lane] = inc - t;
+        if (lane == 15)
+            sh[16] = inc;
     }
     __syncthreads();
     const int res = sh[w] + x - v;
@@ -204,24 +314,17 @@ __device__ unsigned long long block_excl_scan64(unsigned long long v, unsigned l
                                                 unsigned long long *total)
 {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    unsigned long long x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const unsigned long long y = __shfl_up(x, off, 64);
-        if (lane >= off)
-            x += y;
-    }
+    const unsigned long long x = wave_incl_scan64(v);
     if (lane == 63)
         sh[w] = x;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        unsigned long long run = 0;
-        for (int i = 0; i < nw; ++i) {
-            const unsigned long long t = sh[i];
-            sh[i] = run;
-            run += t;
-        }
-        sh[16] = run;
+    if (w == 0) {  // the (at most 16) wave totals, scanned by wave 0
+        const unsigned long long t = lane < nw ? sh[lane] : 0ull;
+        const unsigned long long inc = wave_incl_scan64(t);
+        if (lane < nw)
+            sh[lane] = inc - t;
+        if (lane == 15)
+            sh[16] = inc;
     }
     __syncthreads();
     const unsigned long long res = sh[w] + x - v;
