@@ -558,14 +558,25 @@ int launch_router_logits(const ecf_shape &s, const void *x, const void *wr, int 
     if (T <= 0)
         return ECF_OK;
     ProfScope p("router_logits", st);
-    constexpr int TT = 8;
-    dim3 grid(s.n_experts, (T + TT - 1) / TT);
-    if (s.a_dtype == ECF_BF16)
-        hipLaunchKernelGGL((k_router_logits<true, TT>), grid, dim3(256), 0, st, x, wr, T, s.hidden,
-                           s.n_experts, logits);
+    // Tokens per block: 2 for decode-sized batches (more, shorter blocks: the
+    // kernel is latency-bound there; measured against 1, 4, 8 and 16 at 1, 4 and
+    // 16 tokens), 8 above 32 tokens, where each block re-reading the expert's
+    // router row for only 2 tokens would multiply the cache traffic.
+#define ECF_ROUTER(TTV)                                                                            \
+    {                                                                                              \
+        dim3 grid(s.n_experts, (T + (TTV) - 1) / (TTV));                                           \
+        if (s.a_dtype == ECF_BF16)                                                                 \
+            hipLaunchKernelGGL((k_router_logits<true, TTV>), grid, dim3(256), 0, st, x, wr, T,     \
+                               s.hidden, s.n_experts, logits);                                     \
+        else                                                                                       \
+            hipLaunchKernelGGL((k_router_logits<false, TTV>), grid, dim3(256), 0, st, x, wr, T,    \
+                               s.hidden, s.n_experts, logits);                                     \
+    }
+    if (T <= 32)
+        ECF_ROUTER(2)
     else
-        hipLaunchKernelGGL((k_router_logits<false, TT>), grid, dim3(256), 0, st, x, wr, T, s.hidden,
-                           s.n_experts, logits);
+        ECF_ROUTER(8)
+#undef ECF_ROUTER
     ECF_HIP_CHECK(hipGetLastError());
     return ECF_OK;
 }
