@@ -4,8 +4,8 @@
 // In prefill thousands of tokens reach nearly every expert of a layer
 // (FreeToken paper explainer, section "Wall 1: prefill" -- sparsity vanishes),
 // so each expert is a small dense GEMM: its rows are contiguous in the
-// counting-sort order and tiled BM = 128 rows at a time (the tile list comes
-// from the routing kernels).
+// counting-sort order and tiled BM rows at a time (128 for bf16 weights, 256
+// for MXFP4; the tile list comes from the routing kernels).
 //
 //   GEMM1: [a | b] = X_perm . [W_gate ; W_up]^T, h = silu(a) * b -> H (bf16)
 //          A rows are gathered from x through perm; one block owns 128
@@ -13,9 +13,9 @@
 //          registers on matching accumulator fragments.
 //   GEMM2: Y = H . W_down^T (fp32), combined per token by k_combine.
 //
-// Block = 4 waves (2 x 2), tile 128 rows x BNT weight rows (BNT = 128 for bf16,
-// 256 for MXFP4), BK = 64; each wave owns 64 rows x BNT/2 weight rows (2 x
-// BNT/64 MFMA 32x32 fragments).  Software pipeline of depth 2 through
+// Block = NW waves as WM x (NW / WM), tile BM rows x BNT weight rows, BK = 64
+// (bf16: 4 waves on 128 x 128, each 64 x 64; MXFP4: 8 waves on 256 x 256, each
+// 128 rows x 64 weight rows, i.e. 4 x 2 MFMA 32x32 fragments).  Software pipeline of depth 2 through
 // registers: in program order the loads of k-tile kt+2 come before the MFMAs
 // of k-tile kt and the LDS stores of k-tile kt+1 after them (the compiler's
 // schedule of that order measured faster than pinning it with scheduling
@@ -84,12 +84,13 @@ __device__ __forceinline__ bf16x8_t cvt_mx8(uint32_t w, float s)
 // One stage of global data held in registers between load and LDS store.
 // BNT = weight rows per block tile; NBL = 16-B B chunks per thread and stage.
 // A stage covers KS sub-tiles of BK = 64 reduction elements each.
-template <bool MX, int BM, int BNT, int KS>
+template <bool MX, int BM, int BNT, int KS, int NTH>
 struct Stage {
-    static constexpr int NAL = BM / 32;  // 16-B A chunks per thread and sub-tile
-    static constexpr int NBL = MX ? BNT / 128 : BNT / 32;
-    u32x4_t a[NAL * KS];      // A: rows (tid>>3) + 32q, chunk tid&7, per sub-tile
-    u32x4_t b[NBL * KS];      // B bf16: rows (tid>>3) + 32q; MX: rows (tid>>1) + 128q, half tid&1
+    static constexpr int NAL = BM * 8 / NTH;                // 16-B A chunks per thread and sub-tile
+    static constexpr int NBL = (MX ? BNT * 2 : BNT * 8) / NTH;  // 16-B B chunks per thread and sub-tile
+    static_assert(NAL >= 1 && NBL >= 1, "tile too small for the block");
+    u32x4_t a[NAL * KS];      // A: rows (tid>>3) + (NTH/8)q, chunk tid&7, per sub-tile
+    u32x4_t b[NBL * KS];      // B bf16: rows (tid>>3) + (NTH/8)q; MX: rows (tid>>1) + (NTH/2)q, half tid&1
     uint32_t s;               // MX: the 2*KS scale bytes of row tid (tid < BNT)
 };
 
@@ -104,18 +105,18 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
 }
 
-template <bool MX, int BM, int BNT>
+template <bool MX, int BM, int BNT, int NTH>
 struct Ptrs {
-    uint32_t a[BM / 32];                    // A rows, this thread's 16-B chunk (bytes from A's base)
-    uint32_t b[MX ? BNT / 128 : BNT / 32];  // B rows within the blob, this thread's 16-B chunk
-    uint32_t s;                             // MX: this thread's scale row within the blob
+    uint32_t a[Stage<MX, BM, BNT, 1, NTH>::NAL];  // A rows, this thread's 16-B chunk (bytes from A's base)
+    uint32_t b[Stage<MX, BM, BNT, 1, NTH>::NBL];  // B rows within the blob, this thread's 16-B chunk
+    uint32_t s;                                   // MX: this thread's scale row within the blob
 };
 
-template <bool MX, int BM, int BNT, int KS>
-__device__ __forceinline__ void gload(Stage<MX, BM, BNT, KS> &st, const Ptrs<MX, BM, BNT> &p, rsrc_t ra, rsrc_t rb,
-                                      int kt, int tid)
+template <bool MX, int BM, int BNT, int KS, int NTH>
+__device__ __forceinline__ void gload(Stage<MX, BM, BNT, KS, NTH> &st, const Ptrs<MX, BM, BNT, NTH> &p, rsrc_t ra,
+                                      rsrc_t rb, int kt, int tid)
 {
-    constexpr int NAL = Stage<MX, BM, BNT, KS>::NAL, NBL = Stage<MX, BM, BNT, KS>::NBL;
+    constexpr int NAL = Stage<MX, BM, BNT, KS, NTH>::NAL, NBL = Stage<MX, BM, BNT, KS, NTH>::NBL;
 #pragma unroll
     for (int sub = 0; sub < KS; ++sub) {
         const int col = (kt * KS + sub) * BK;  // first reduction element of the sub-tile
@@ -139,26 +140,26 @@ __device__ __forceinline__ void gload(Stage<MX, BM, BNT, KS> &st, const Ptrs<MX,
 // Bs + sub * (B tile size).  MX scales are widened to fp32 here, once per row
 // and stage, and stored group-major: Scf[group * (BNT + 32) + row] (the pad
 // puts the two lane halves' reads on different banks).
-template <bool MX, int BM, int BNT, int KS>
-__device__ __forceinline__ void sstore(const Stage<MX, BM, BNT, KS> &st, u32x4_t *As, u32x4_t *Bs, float *Scf,
+template <bool MX, int BM, int BNT, int KS, int NTH>
+__device__ __forceinline__ void sstore(const Stage<MX, BM, BNT, KS, NTH> &st, u32x4_t *As, u32x4_t *Bs, float *Scf,
                                        int tid)
 {
-    constexpr int NAL = Stage<MX, BM, BNT, KS>::NAL, NBL = Stage<MX, BM, BNT, KS>::NBL;
+    constexpr int NAL = Stage<MX, BM, BNT, KS, NTH>::NAL, NBL = Stage<MX, BM, BNT, KS, NTH>::NBL;
     constexpr int BT = MX ? BNT * 2 : BNT * 8;  // 16-B slots of one B sub-tile
 #pragma unroll
     for (int sub = 0; sub < KS; ++sub) {
 #pragma unroll
         for (int q = 0; q < NAL; ++q)
-            As[sub * BM * 8 + swz((tid >> 3) + 32 * q, tid & 7)] = st.a[sub * NAL + q];
+            As[sub * BM * 8 + swz((tid >> 3) + (NTH / 8) * q, tid & 7)] = st.a[sub * NAL + q];
 #pragma unroll
         for (int q = 0; q < NBL; ++q) {
             if (MX)
-                Bs[sub * BT + mx_slot((tid >> 1) + 128 * q, tid & 1)] = st.b[sub * NBL + q];
+                Bs[sub * BT + mx_slot((tid >> 1) + (NTH / 2) * q, tid & 1)] = st.b[sub * NBL + q];
             else
-                Bs[sub * BT + swz((tid >> 3) + 32 * q, tid & 7)] = st.b[sub * NBL + q];
+                Bs[sub * BT + swz((tid >> 3) + (NTH / 8) * q, tid & 7)] = st.b[sub * NBL + q];
         }
     }
-    if (MX && (BNT >= 256 || tid < BNT)) {
+    if (MX && (BNT >= NTH || tid < BNT)) {
         // The empty asm keeps the widening here, after the stage's other stores:
         // left free, the compiler hoists it next to the load, and waiting for
         // that load there waits for every load issued before it.
@@ -197,14 +198,16 @@ struct IC {
 // and B alike, so every chunk is used once.  Lane half g then reads the 32
 // MXFP4 elements 32g..32g+31 -- 16 bytes, exactly one E8M0 scale group -- with
 // a single LDS read per k-tile.
-template <int MODE, bool MX, int BM, int BNT, int MINB, int KS, int WM>
-__global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
+template <int MODE, bool MX, int BM, int BNT, int MINB, int KS, int WM, int NW>
+__global__ __launch_bounds__(64 * NW, MINB) void k_grouped_gemm(
     const uint64_t *__restrict__ ptrs, size_t off_w0, size_t off_w1, size_t off_s0, size_t off_s1,
     const int32_t *__restrict__ tiles, const int32_t *__restrict__ n_tiles,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm, const uint16_t *__restrict__ A,
     int K, int N, int lda, int k, int E, int R, int NT, uint32_t blob_bytes, void *__restrict__ out)
 {
-    constexpr int NCB = BNT / 64;  // 32-column MFMA blocks per wave
+    constexpr int NTH = 64 * NW, WN = NW / WM, WROWS = BM / WM, NMSMAX = WROWS / 32;
+    constexpr int NCB = BNT / (32 * WN);  // 32-column MFMA blocks per wave
+    static_assert(NW % WM == 0 && NCB >= (MODE == 1 ? 2 : 1) && NMSMAX >= 1, "wave layout");
     constexpr int BT = MX ? BNT * 2 : BNT * 8;  // 16-B slots of one B sub-tile
     __shared__ u32x4_t As[2][KS * BM * 8];
     __shared__ u32x4_t Bs[2][KS * BT];
@@ -222,17 +225,16 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
     const int mrows = min(BM, offsets[e + 1] - rb);
     if (!blob || m0 < 0 || rb < 0 || mrows <= 0 || rb + mrows > R)
         return;
-    // WM waves along M (2: 2 x 2 layout, 64 rows per wave; 1: 1 x 4, 128 rows per
-    // wave, which halves the per-MFMA B-fragment work at the cost of A reads)
-    constexpr int WN = 4 / WM, WROWS = BM / WM, NMSMAX = WROWS / 32;
+    // NW waves, WM of them along M (4 waves as 2 x 2: 64 rows per wave; WM = 1
+    // halves the per-MFMA B-fragment work at the cost of A reads)
     const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, wm = w / WN, wn = w % WN, g = l >> 5;
     // MODE 1: this block's intermediate columns [n0, n0 + BNT/2); MODE 2: outputs [n0, n0 + BNT)
     const int n0 = nt * (MODE == 1 ? BNT / 2 : BNT);
 
-    Ptrs<MX, BM, BNT> p;
+    Ptrs<MX, BM, BNT, NTH> p;
 #pragma unroll
-    for (int q = 0; q < BM / 32; ++q) {
-        const int row = min((tid >> 3) + 32 * q, mrows - 1);
+    for (int q = 0; q < Stage<MX, BM, BNT, 1, NTH>::NAL; ++q) {
+        const int row = min((tid >> 3) + (NTH / 8) * q, mrows - 1);
         const size_t arow = MODE == 1 ? (size_t)(perm[rb + row] / k) : (size_t)row;  // from abase
         p.a[q] = (uint32_t)(arow * lda * 2 + (tid & 7) * 16);
     }
@@ -254,9 +256,9 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
     };
     if (MX) {
 #pragma unroll
-        for (int q = 0; q < (MX ? BNT / 128 : BNT / 32); ++q) {
+        for (int q = 0; q < Stage<MX, BM, BNT, 1, NTH>::NBL; ++q) {
             size_t so, sco;
-            const int r = brow((tid >> 1) + 128 * q, so, sco);
+            const int r = brow((tid >> 1) + (NTH / 2) * q, so, sco);
             p.b[q] = (uint32_t)(so + (size_t)r * (K / 2) + (tid & 1) * 16);
         }
         size_t so, sco;
@@ -264,9 +266,9 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
         p.s = (uint32_t)(sco + (size_t)r * (K / 32));
     } else {
 #pragma unroll
-        for (int q = 0; q < (MX ? BNT / 128 : BNT / 32); ++q) {
+        for (int q = 0; q < Stage<MX, BM, BNT, 1, NTH>::NBL; ++q) {
             size_t so, sco;
-            const int r = brow((tid >> 3) + 32 * q, so, sco);
+            const int r = brow((tid >> 3) + (NTH / 8) * q, so, sco);
             p.b[q] = (uint32_t)(so + (size_t)r * K * 2 + (tid & 7) * 16);
         }
         p.s = 0;
@@ -292,10 +294,10 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
 #pragma unroll
                 for (int j = 0; j < 16; ++j)
                     acc[a][b][j] = 0.f;
-        Stage<MX, BM, BNT, KS> s0, s1;
-        gload<MX, BM, BNT, KS>(s0, p, ra, rbs, 0, tid);
-        gload<MX, BM, BNT, KS>(s1, p, ra, rbs, 1, tid);
-        sstore<MX, BM, BNT, KS>(s0, As[0], Bs[0], Scf[0], tid);
+        Stage<MX, BM, BNT, KS, NTH> s0, s1;
+        gload(s0, p, ra, rbs, 0, tid);
+        gload(s1, p, ra, rbs, 1, tid);
+        sstore(s0, As[0], Bs[0], Scf[0], tid);
         __syncthreads();
         // NXT holds k-tile kt+1 (loaded one iteration ago); FRE is free and
         // receives k-tile kt+2.  Two copies of the body alternate the roles so
@@ -307,7 +309,7 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
 #define ECF_GEMM_BODY(KT, NXT, FRE)                                                                  \
     {                                                                                               \
         const int cur = (KT) & 1;                                                                   \
-        gload<MX, BM, BNT, KS>(FRE, p, ra, rbs, min((KT) + 2, nk - 1), tid);                        \
+        gload(FRE, p, ra, rbs, min((KT) + 2, nk - 1), tid);                                         \
         if (NMS > 0) {                                                                              \
             _Pragma("unroll") for (int sub = 0; sub < KS; ++sub)                                    \
             {                                                                                       \
@@ -333,7 +335,7 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
                 }                                                                                   \
             }                                                                                       \
         }                                                                                           \
-        sstore<MX, BM, BNT, KS>(NXT, As[cur ^ 1], Bs[cur ^ 1], Scf[cur ^ 1], tid);                  \
+        sstore(NXT, As[cur ^ 1], Bs[cur ^ 1], Scf[cur ^ 1], tid);                                   \
         __syncthreads();                                                                            \
     }
         for (int kt = 0; kt < nk; kt += 2) {
@@ -392,11 +394,13 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
 // ---------------------------------------------------------------------------------
 
 // Tile choice per weight format, measured on MI355X (bf16: 4096-token layer,
-// d 4096, I 1024, top-6; MXFP4: 8192-token layer, I 2048, top-8): two blocks
-// per CU, one 64-wide sub-tile per stage, 2 x 2 waves; 128 weight rows per
-// N-tile for bf16 (HBM-bound there), 256 for MXFP4 (halves the A re-reads and
-// the per-row MFMA overheads).  Two-sub-tile stages, a 1 x 4 wave layout, three
-// blocks per CU and expanding MXFP4 to bf16 once at the LDS store were each
+// d 4096, I 1024, top-6; MXFP4: 8192-token layer, I 2048, top-8).  bf16 (HBM-
+// bound): 128 x 128 tiles, 4 waves as 2 x 2, two blocks per CU.  MXFP4: 256 x
+// 256 tiles, 8 waves as 2 x 4 (128 rows x 64 weight rows each), one block per
+// CU -- each expanded B fragment feeds four MFMAs and the weights stream once
+// per 256 rows; GEMM1 5% faster than 128 x 256 tiles with 4 waves.  Two-sub-tile
+// stages, a 1 x 4 wave layout, three blocks per CU, expanding MXFP4 to bf16 once
+// at the LDS store, 4 waves on 256 x 256 and 8 waves on 128 x 256 were each
 // slower or spilled registers.
 #ifndef ECF_BF16_BNT
 #define ECF_BF16_BNT 128
@@ -404,12 +408,19 @@ __global__ __launch_bounds__(256, MINB) void k_grouped_gemm(
 #define ECF_BF16_KS 1
 #define ECF_BF16_WM 2
 #endif
+#ifndef ECF_BF16_NW
+#define ECF_BF16_NW 4
+#endif
 #ifndef ECF_MX_BNT
 #define ECF_MX_BNT 256
-#define ECF_MX_MINB 2
+#define ECF_MX_MINB 1
 #define ECF_MX_KS 1
 #define ECF_MX_WM 2
 #endif
+#ifndef ECF_MX_NW
+#define ECF_MX_NW 8
+#endif
+
 
 int launch_prefill_gemm1(const ecf_shape &s, const ExpertTables &ex, const RouteOut &o, const void *x,
                          int T, uint16_t *H, hipStream_t st)
@@ -423,17 +434,18 @@ int launch_prefill_gemm1(const ecf_shape &s, const ExpertTables &ex, const Route
                          "be under 4 GiB", T, s.hidden, ex.lay.bytes);
     const int nblk = max_tiles(s, T) * NT;
     ProfScope p("prefill_gemm1", st);
-#define ECF_G1(MXV, BNV, MBV, KSV, WMV)                                                                    \
-    hipLaunchKernelGGL((k_grouped_gemm<1, MXV, (MXV) ? ECF_MX_BM : kPrefillMT, BNV, MBV, KSV, WMV>), dim3(nblk), dim3(256), 0, st, ex.ptrs,  \
+#define ECF_G1(MXV, BNV, MBV, KSV, WMV, NWV)                                                               \
+    hipLaunchKernelGGL((k_grouped_gemm<1, MXV, (MXV) ? ECF_MX_BM : kPrefillMT, BNV, MBV, KSV, WMV, NWV>), dim3(nblk), \
+                       dim3(64 * (NWV)), 0, st, ex.ptrs,                                                     \
                        ex.lay.off[0], ex.lay.off[1], ex.lay.off[3], ex.lay.off[4], o.tiles, o.n_tiles,         \
                        o.offsets, o.perm, (const uint16_t *)x, s.hidden, s.inter, s.hidden, s.top_k,         \
                        s.n_experts, T * s.top_k, NT, (uint32_t)ex.lay.bytes, (void *)H)
     // K = d; the main loop takes an even number of stages of KS sub-tiles: d % (128 * KS) == 0
     // (d is a multiple of 256)
     if (mx)
-        ECF_G1(true, ECF_MX_BNT, ECF_MX_MINB, ECF_MX_KS, ECF_MX_WM);
+        ECF_G1(true, ECF_MX_BNT, ECF_MX_MINB, ECF_MX_KS, ECF_MX_WM, ECF_MX_NW);
     else
-        ECF_G1(false, ECF_BF16_BNT, ECF_BF16_MINB, ECF_BF16_KS, ECF_BF16_WM);
+        ECF_G1(false, ECF_BF16_BNT, ECF_BF16_MINB, ECF_BF16_KS, ECF_BF16_WM, ECF_BF16_NW);
 #undef ECF_G1
     ECF_HIP_CHECK(hipGetLastError());
     return ECF_OK;
@@ -449,8 +461,9 @@ int launch_prefill_gemm2(const ecf_shape &s, const ExpertTables &ex, const Route
         return set_error(ECF_EUNSUPPORTED, "prefill path: one expert blob (%zu B) must be under 4 GiB", ex.lay.bytes);
     const int nblk = max_tiles(s, T) * NT;
     ProfScope p("prefill_gemm2", st);
-#define ECF_G2(MXV, BNV, MBV, KSV, WMV)                                                                    \
-    hipLaunchKernelGGL((k_grouped_gemm<2, MXV, (MXV) ? ECF_MX_BM : kPrefillMT, BNV, MBV, KSV, WMV>), dim3(nblk), dim3(256), 0, st, ex.ptrs,  \
+#define ECF_G2(MXV, BNV, MBV, KSV, WMV, NWV)                                                               \
+    hipLaunchKernelGGL((k_grouped_gemm<2, MXV, (MXV) ? ECF_MX_BM : kPrefillMT, BNV, MBV, KSV, WMV, NWV>), dim3(nblk), \
+                       dim3(64 * (NWV)), 0, st, ex.ptrs,                                                     \
                        ex.lay.off[2], ex.lay.off[2], ex.lay.off[5], ex.lay.off[5], o.tiles, o.n_tiles,         \
                        o.offsets, o.perm, H, s.inter, s.hidden, s.inter, s.top_k, s.n_experts, T * s.top_k,  \
                        NT, (uint32_t)ex.lay.bytes, (void *)Y)
@@ -458,14 +471,14 @@ int launch_prefill_gemm2(const ecf_shape &s, const ExpertTables &ex, const Route
     // only when I % 256 == 0 (I % 128 == 0 holds on this path)
     if (mx) {
         if (s.inter % (128 * ECF_MX_KS) == 0)
-            ECF_G2(true, ECF_MX_BNT, ECF_MX_MINB, ECF_MX_KS, ECF_MX_WM);
+            ECF_G2(true, ECF_MX_BNT, ECF_MX_MINB, ECF_MX_KS, ECF_MX_WM, ECF_MX_NW);
         else
-            ECF_G2(true, ECF_MX_BNT, ECF_MX_MINB, 1, ECF_MX_WM);
+            ECF_G2(true, ECF_MX_BNT, ECF_MX_MINB, 1, ECF_MX_WM, ECF_MX_NW);
     } else {
         if (s.inter % (128 * ECF_BF16_KS) == 0)
-            ECF_G2(false, ECF_BF16_BNT, ECF_BF16_MINB, ECF_BF16_KS, ECF_BF16_WM);
+            ECF_G2(false, ECF_BF16_BNT, ECF_BF16_MINB, ECF_BF16_KS, ECF_BF16_WM, ECF_BF16_NW);
         else
-            ECF_G2(false, ECF_BF16_BNT, ECF_BF16_MINB, 1, ECF_BF16_WM);
+            ECF_G2(false, ECF_BF16_BNT, ECF_BF16_MINB, 1, ECF_BF16_WM, ECF_BF16_NW);
     }
 #undef ECF_G2
     ECF_HIP_CHECK(hipGetLastError());
