@@ -187,7 +187,26 @@ def bench_decode(torch, ecf, syn, Ts, steps, warmup, n_batches=64, use_graph=Tru
         log(f"decode {w_dtype} T={T}: {ms / steps * 1e3:.1f} us/step, {results[T]['tokens_per_s']:.0f} tok/s, "
             f"U={U_avg:.1f}, layer {results[T]['layer_GBps']:.0f} GB/s, gate/up {results[T]['gateup_GBps']:.0f} GB/s")
         del graphs
-    sample = dict(pool=pool, wr=wr, cfg=cfg)
+    def gpu_run(x_cpu):
+        """One eager forward of the layer on x (host tensor); routing and output on the host."""
+        T = x_cpu.shape[0]
+        x = x_cpu.to("cuda")
+        out = torch.empty((T, d), dtype=torch.float32, device="cuda")
+        idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        gate = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        cnt = torch.empty(E, dtype=torch.int32, device="cuda")
+        perm = torch.empty(T * k, dtype=torch.int32, device="cuda")
+        lgo = torch.empty((T, E), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            a = lay.args(router_w=wr, expert_ptrs=pool.ptrs, stream=stream, topk_idx=idx, topk_gate=gate,
+                         counts=cnt, perm=perm, logits_out=lgo)
+            lay.forward(a, x, out, want_stats=False)
+        stream.synchronize()
+        return dict(idx=idx.cpu().numpy(), gate=gate.cpu().numpy(), counts=cnt.cpu().numpy(),
+                    perm=perm.cpu().numpy(), out=out.cpu().numpy(), logits=lgo.cpu().numpy())
+
+    sample = dict(pool=pool, wr=wr, cfg=cfg, gpu_run=gpu_run if w_dtype == "bf16" else None)
     return results, sample
 
 
@@ -214,6 +233,13 @@ def cpu_baseline_decode(torch, syn, sample, budget_s=15.0, T=16, max_batches=256
                         for nm, off in shape_sections.items()}
         return cache[e]
 
+    # every timed batch is also run on the GPU and compared with the oracle: routing
+    # exactly (rows whose fp32 logits agree; the others may differ by one ulp),
+    # counts and permutation exactly where every row agrees, outputs within
+    # 2e-2 x the oracle output's RMS
+    gpu_run = sample.get("gpu_run")
+    chk = dict(batches=0, tokens=0, rows_logit_1ulp=0, rows_routing_exact=0, batches_perm_counts_exact=0,
+               max_err_over_rms=0.0, tolerance=2e-2, ok=True)
     done, elapsed, batches = 0, 0.0, 0
     while elapsed < budget_s and batches < max_batches:
         x = syn.activations(cfg, T, batch=batches)
@@ -228,10 +254,40 @@ def cpu_baseline_decode(torch, syn, sample, budget_s=15.0, T=16, max_batches=256
         done += T
         batches += 1
         assert np.all(np.isfinite(res["out"]))
+        if gpu_run is not None:
+            gr = gpu_run(x)
+            same = np.all(gr["logits"] == res["logits"], axis=1)
+            ulp = np.spacing(np.abs(res["logits"]).astype(np.float32))
+            exact = same & np.all(gr["idx"] == res["idx"], axis=1)
+            perm_ok = bool(same.all() and np.array_equal(gr["counts"], res["counts"])
+                           and np.array_equal(gr["perm"], res["perm"]))
+            rms = float(np.sqrt(np.mean(res["out"] ** 2)))
+            err = float(np.max(np.abs(gr["out"] - res["out"]))) / rms
+            chk["batches"] += 1
+            chk["tokens"] += T
+            chk["rows_logit_1ulp"] += int((~same).sum())
+            chk["rows_routing_exact"] += int(exact.sum())
+            chk["batches_perm_counts_exact"] += int(perm_ok)
+            chk["max_err_over_rms"] = max(chk["max_err_over_rms"], err)
+            chk["ok"] = chk["ok"] and bool(np.all(np.abs(gr["logits"] - res["logits"]) <= ulp)) \
+                and int(exact.sum()) == int(same.sum()) and (perm_ok or not same.all()) and err <= 2e-2
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": done / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{batches} batches of {T} tokens of the headline decode workload (router, top-k, "
-                      f"permutation, experts, combine in fp64), {elapsed:.1f} s of CPU time"}
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
+    out = {"value": done / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{batches} batches of {T} tokens of the headline decode workload (router, top-k, "
+                     f"permutation, experts, combine in fp64), {elapsed:.1f} s of CPU time",
+           "cpu_model": model, "nproc": os.cpu_count(), "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+    if gpu_run is not None:
+        out["checked_against_gpu"] = chk
+        log(f"cpu baseline: GPU layer checked on the same {chk['batches']} batches: routing exact on "
+            f"{chk['rows_routing_exact']}/{chk['tokens']} tokens ({chk['rows_logit_1ulp']} with 1-ulp logits), "
+            f"max|err|/RMS {chk['max_err_over_rms']:.2e}, {'ok' if chk['ok'] else 'FAILED'}")
+    return out
 
 
 # ---- prefill (bf16 and MXFP4) ----------------------------------------------------------------
