@@ -163,6 +163,14 @@ def bench_decode(torch, ecf, syn, Ts, steps, warmup, n_batches=64, use_graph=Tru
             stream.synchronize()
             torch.cuda.synchronize()
             ms = ev0.elapsed_time(ev1)
+            # per-step spread: the same steps again with an event between steps
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+            evs[0].record(stream)
+            for i in range(steps):
+                step(i)
+                evs[i + 1].record(stream)
+            stream.synchronize()
+            per_step = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(steps))
             # per-kernel durations: same steps again, eager, each launch bracketed by HIP events
             ecf.ecf_profile_reset()
             ecf.ecf_profile_enable(True)
@@ -180,11 +188,14 @@ def bench_decode(torch, ecf, syn, Ts, steps, warmup, n_batches=64, use_graph=Tru
         gu_us = kern["decode_gateup"]["avg_us"]
         results[T] = dict(
             tokens=T, ms_per_step=ms / steps, tokens_per_s=T * steps / (ms / 1e3), unique_experts_avg=U_avg,
+            us_step_median=per_step[steps // 2], us_step_p10=per_step[steps // 10],
+            us_step_p90=per_step[min(steps - 1, (9 * steps) // 10)],
             layer_bytes=layer_bytes, layer_GBps=layer_bytes / (ms / steps * 1e-3) / 1e9,
             layer_hbm_frac=layer_bytes / (ms / steps * 1e-3) / 1e9 / HBM_PEAK_GBS,
             gateup_bytes=gu_bytes, gateup_avg_us=gu_us, gateup_GBps=gu_bytes / (gu_us * 1e-6) / 1e9,
             kernels=kern, graph=use_graph)
-        log(f"decode {w_dtype} T={T}: {ms / steps * 1e3:.1f} us/step, {results[T]['tokens_per_s']:.0f} tok/s, "
+        log(f"decode {w_dtype} T={T}: {ms / steps * 1e3:.1f} us/step (median {per_step[steps // 2]:.1f}), "
+            f"{results[T]['tokens_per_s']:.0f} tok/s, "
             f"U={U_avg:.1f}, layer {results[T]['layer_GBps']:.0f} GB/s, gate/up {results[T]['gateup_GBps']:.0f} GB/s")
         del graphs
     def gpu_run(x_cpu):
@@ -320,6 +331,13 @@ def bench_prefill(torch, ecf, syn, name, steps, warmup):
     ev1.record()
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / steps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
+    for i in range(steps):
+        assert call(i) == 0
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
     ecf.ecf_profile_reset()
     ecf.ecf_profile_enable(True)
     for i in range(steps):
@@ -333,6 +351,8 @@ def bench_prefill(torch, ecf, syn, name, steps, warmup):
     n_active = int((counts > 0).sum())
     wbytes = n_active * S
     res = dict(tokens=T, ms_per_layer=ms, tokens_per_s=T / (ms * 1e-3), active_experts=n_active,
+               ms_median=per_step[steps // 2], ms_p10=per_step[steps // 10],
+               ms_p90=per_step[min(steps - 1, (9 * steps) // 10)],
                tflops=flops / (ms * 1e-3) / 1e12, mfma_frac=flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                weight_GBps=wbytes / (ms * 1e-3) / 1e9, hbm_frac_weights=wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                kernels=kern)
@@ -341,7 +361,8 @@ def bench_prefill(torch, ecf, syn, name, steps, warmup):
     if g1 and g2:
         res["gemm1_tflops"] = 2.0 * R * d * 2 * I / (g1 * 1e-6) / 1e12
         res["gemm2_tflops"] = 2.0 * R * I * d / (g2 * 1e-6) / 1e12
-    log(f"{name}: {ms:.3f} ms/layer, {res['tokens_per_s']:.0f} tok/s, {res['tflops']:.0f} TFLOP/s "
+    log(f"{name}: {ms:.3f} ms/layer (median {per_step[steps // 2]:.3f}), {res['tokens_per_s']:.0f} tok/s, "
+        f"{res['tflops']:.0f} TFLOP/s "
         f"({100 * res['mfma_frac']:.1f}% MFMA), weights {res['weight_GBps']:.0f} GB/s")
     del pool
     torch.cuda.empty_cache()
@@ -626,10 +647,10 @@ def main():
         also.update({f"decode_mxfp4_T{T}": dec4[T] for T in dec4})
         torch.cuda.empty_cache()
     if "prefill" in wl:
-        also["prefill_bf16_T4096"] = bench_prefill(torch, ecf, syn, "prefill", max(5, args.steps // 20),
+        also["prefill_bf16_T4096"] = bench_prefill(torch, ecf, syn, "prefill", max(20, args.steps // 10),
                                                    max(2, args.warmup // 5))
     if "prefill_fp4" in wl:
-        also["prefill_mxfp4_T8192"] = bench_prefill(torch, ecf, syn, "prefill_fp4", max(5, args.steps // 20),
+        also["prefill_mxfp4_T8192"] = bench_prefill(torch, ecf, syn, "prefill_fp4", max(20, args.steps // 10),
                                                     max(2, args.warmup // 5))
     if sample is not None and not args.no_cpu_baseline:
         log("cpu baseline: oracle on sampled decode batches")
