@@ -605,6 +605,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--cached-steps", type=int, default=12)
+    ap.add_argument("--cached-warmup", type=int, default=None, help="cached decode warm-up steps (default: --cached-steps)")
+    ap.add_argument("--policies", default=",".join(POLICIES), help="policies the 'policies' workload compares")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run one plain 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--host-inputs", action="store_true",
@@ -661,7 +663,8 @@ def main():
     if "prefetch" in wl:
         also["prefill_prefetch_stack"] = bench_prefetch(torch, ecf, syn)
     if wl & {"cached", "bandwidth", "policies"}:
-        ctx = cached_setup(torch, ecf, syn, steps=args.cached_steps, warmup=args.cached_steps)
+        cw = args.cached_steps if args.cached_warmup is None else args.cached_warmup
+        ctx = cached_setup(torch, ecf, syn, steps=args.cached_steps, warmup=cw)
         bw = None
         if wl & {"bandwidth", "policies"}:
             bw = also["bandwidth_profile"] = bench_bandwidth(torch, ecf, ctx)
@@ -669,14 +672,16 @@ def main():
             also["cached_decode_43L_T16"] = bench_cached(torch, ecf, syn, ctx, "lru_qstar")
         if "policies" in wl:
             pol = {p: (dict(also["cached_decode_43L_T16"]) if p == "lru_qstar" and "cached" in wl
-                       else bench_cached(torch, ecf, syn, ctx, p, bw)) for p in POLICIES}
+                       else bench_cached(torch, ecf, syn, ctx, p, bw))
+                   for p in POLICIES if p in args.policies.split(",")}
             for r in pol.values():
                 r.pop("q_hist")
             also["cached_policies_43L_T16"] = pol
         del ctx
         torch.cuda.empty_cache()
     if "cached_fp4" in wl:
-        ctx = cached_setup(torch, ecf, syn, steps=args.cached_steps, warmup=args.cached_steps, w_dtype="mxfp4")
+        cw = args.cached_steps if args.cached_warmup is None else args.cached_warmup
+        ctx = cached_setup(torch, ecf, syn, steps=args.cached_steps, warmup=cw, w_dtype="mxfp4")
         bw4 = also["bandwidth_profile_mxfp4"] = bench_bandwidth(torch, ecf, ctx)
         for p in ("lru_qstar", "lru_qstar_measured"):
             r = bench_cached(torch, ecf, syn, ctx, p, bw4)
