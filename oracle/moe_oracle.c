@@ -100,6 +100,13 @@ void orc_logits(int a_dtype, const void *x, const void *wr, int T, int d, int E,
         }
 }
 
+/* A logit as routing reads it: NaN is taken as -infinity (in the order and in
+ * the softmax); -0 and +0 compare equal. */
+static double route_val(float v)
+{
+    return isnan(v) ? -INFINITY : (double)v;
+}
+
 /* Top-k and gates for every token.
  * Selection: k rounds, each taking the largest logit not yet taken; a strict
  * ">" comparison in ascending id order keeps the lower expert id on ties.
@@ -114,22 +121,22 @@ void orc_route(const float *logits, int T, int E, int k, int renorm, int32_t *id
         for (int j = 0; j < k; ++j) {
             int best = -1;
             for (int e = 0; e < E; ++e)
-                if (!taken[e] && (best < 0 || l[e] > l[best]))
+                if (!taken[e] && (best < 0 || route_val(l[e]) > route_val(l[best])))
                     best = e;
             taken[best] = 1;
             idx[(long)t * k + j] = best;
         }
         free(taken);
-        double mx = (double)l[idx[(long)t * k]];
+        double mx = route_val(l[idx[(long)t * k]]);
         double denom = 0.0;
         if (renorm)
             for (int j = 0; j < k; ++j)
-                denom += exp((double)l[idx[(long)t * k + j]] - mx);
+                denom += exp(route_val(l[idx[(long)t * k + j]]) - mx);
         else
             for (int e = 0; e < E; ++e)
-                denom += exp((double)l[e] - mx);
+                denom += exp(route_val(l[e]) - mx);
         for (int j = 0; j < k; ++j)
-            gates[(long)t * k + j] = exp((double)l[idx[(long)t * k + j]] - mx) / denom;
+            gates[(long)t * k + j] = exp(route_val(l[idx[(long)t * k + j]]) - mx) / denom;
     }
 }
 

@@ -90,6 +90,35 @@ def test_tied_logits_pick_lowest_ids():
     compare(res, c.oracle(), TOL["bf16"], "ties")
 
 
+@pytest.mark.parametrize("T,renorm", [(20, 1), (20, 0), (600, 1), (600, 0)])
+def test_special_logits(T, renorm):
+    """NaN logits rank as -inf (in the order and in the softmax), -0 ties +0 with
+    the lower id first, and -inf entries are picked after every finite logit, in
+    id order: on the single-block routing kernel (T*k <= 2048, decode path) and
+    on the multi-block top-k and counting sort (T*k > 2048, prefill path)."""
+    E, k = 16, 4
+    cfg = cfg_small(experts=E, top_k=k, cid=140)
+    rng = np.random.default_rng(140 + T)
+    lg = rng.normal(0, 1, (T, E)).astype(np.float32)
+    for t in range(T):
+        r = t % 4
+        if r == 0:  # NaN at the lowest id and inside the range
+            lg[t, [0, 7]] = np.nan
+        elif r == 1:  # the two largest tie at -0 (id 3) and +0 (id 9)
+            lg[t] = -np.abs(lg[t]) - 1.0
+            lg[t, 3], lg[t, 9] = -0.0, 0.0
+        elif r == 2:  # three finite logits: the fourth pick is the lowest-id -inf / NaN entry
+            lg[t] = -np.inf
+            lg[t, [2, 5, 11]] = [0.3, -0.1, 0.3]
+            lg[t, 1] = np.nan
+    say(f"case: special logits T={T} renorm={renorm}")
+    c = Case(cfg, T, renorm=renorm, logits=torch.from_numpy(lg))
+    res = c.run(path=ecf.ECF_PATH_PREFILL if T > 64 else ecf.ECF_PATH_DECODE)
+    ref = c.oracle()
+    assert list(ref["idx"][1][:2]) == [3, 9] and list(ref["idx"][2]) == [2, 11, 5, 0]
+    compare(res, ref, TOL["bf16"], f"special logits T={T} renorm={renorm}")
+
+
 def test_no_renorm_gates():
     cfg = cfg_small(cid=61)
     c = Case(cfg, 6, renorm=0)

@@ -112,6 +112,23 @@ def test_topk_against_full_sort(E, k):
         assert list(idx[t]) == list(order[:k])
 
 
+def test_special_logits_hand_derived():
+    """NaN ranks as -inf in the order and the softmax, -0 ties with +0 (lower id
+    first), -inf is selectable after every finite logit; values derived by hand."""
+    nan, inf = np.float32(np.nan), np.float32(np.inf)
+    lg = np.array([[nan, 1.0, 0.5, nan, -inf, -0.0, 0.0, -2.0]], np.float32)
+    idx, g = oracle.route(lg, 8, renorm=True)
+    # 1, 0.5, -0 (id 5) and +0 (id 6) tie -> 5 first, -2, then -inf, NaN, NaN as -inf in id order
+    assert list(idx[0]) == [1, 2, 5, 6, 7, 0, 3, 4]
+    z = 1.0 + np.exp(-0.5) + 2 * np.exp(-1.0) + np.exp(-3.0)
+    want = np.array([1.0, np.exp(-0.5), np.exp(-1.0), np.exp(-1.0), np.exp(-3.0), 0, 0, 0]) / z
+    assert np.allclose(g[0], want, rtol=1e-15, atol=0)
+    # renorm=0: the NaN entries add nothing to the full softmax either
+    idx2, g2 = oracle.route(lg, 2, renorm=False)
+    assert list(idx2[0]) == [1, 2]
+    assert np.allclose(g2[0], [1.0 / z, np.exp(-0.5) / z], rtol=1e-15, atol=0)
+
+
 def test_gates_against_library_softmax():
     rng = _rng(7)
     lg = rng.normal(0, 2, (30, 32)).astype(np.float32)
