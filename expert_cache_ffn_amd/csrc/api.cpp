@@ -1,6 +1,7 @@
 // C-ABI entry points of libecf: errors, layouts, workspace, prefetch, profiling
 // hooks and the layer forward (all-resident and expert-cache modes).
 #include <algorithm>
+#include <atomic>
 #include <chrono>
 #include <cmath>
 #include <cstdarg>
@@ -44,7 +45,7 @@ struct Pending {
     hipEvent_t a, b;
 };
 std::mutex g_prof_mu;
-bool g_prof_on = false;
+std::atomic<bool> g_prof_on{false};  // read by every launch, on any thread
 std::vector<ProfAcc> g_prof;
 std::vector<Pending> g_pending;
 
@@ -244,7 +245,7 @@ int ecf_expert_layout(const ecf_shape *shape, size_t offsets_out[6])
 
 size_t ecf_workspace_bytes(const ecf_shape *shape, int32_t max_tokens)
 {
-    if (check_shape(shape) != ECF_OK || max_tokens < 0)
+    if (check_shape(shape) != ECF_OK || max_tokens < 0 || (int64_t)max_tokens * shape->top_k > kMaxRows)
         return 0;
     return ws_layout(*shape, max_tokens).total;
 }
@@ -531,8 +532,8 @@ int moe_layer_forward(const ecf_layer_args *a, const void *d_x, int32_t T, float
         if (rc != ECF_OK)
             return rc;
         const ecf_shape &s = a->shape;
-        if (T < 0)
-            return set_error(ECF_EINVAL, "n_tokens < 0");
+        if (T < 0 || (int64_t)T * s.top_k > kMaxRows)
+            return set_error(ECF_EINVAL, "n_tokens must be in [0, %lld / top_k] (got %d)", (long long)kMaxRows, T);
         if (stats)
             std::memset(stats, 0, sizeof *stats);
         if (T == 0)

@@ -47,6 +47,7 @@ struct ProfScope {
 };
 
 // ---- geometry ------------------------------------------------------------------
+constexpr int64_t kMaxRows = (int64_t)1 << 26;  // n_tokens * top_k per call (row indices are 32-bit)
 constexpr int kSortSeg = 1024;      // rows per segment of the multi-block counting sort
 constexpr int kSmallRouteRows = 2048; // R up to this uses the single-block routing kernel
 constexpr int kPrefillMT = 128;     // rows per prefill GEMM tile (bf16 weights)

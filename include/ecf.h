@@ -87,7 +87,8 @@ typedef struct {
 size_t ecf_expert_bytes(const ecf_shape *shape);
 int ecf_expert_layout(const ecf_shape *shape, size_t offsets_out[6]);
 
-/* Device workspace bytes a forward call needs for up to max_tokens tokens. */
+/* Device workspace bytes a forward call needs for up to max_tokens tokens
+ * (0 for an invalid shape or max_tokens * top_k above 2^26). */
 size_t ecf_workspace_bytes(const ecf_shape *shape, int32_t max_tokens);
 
 /* ---- q* split [TF "Bandwidth-adaptive execution (q* policy)"] ----------------
@@ -111,7 +112,7 @@ int32_t qstar_split(int32_t m, double b_p, double b_h);
  * (the source of truth; entries may alias), or h_pool may be NULL if the
  * caller never asks the library to copy or host-compute experts.
  * host_threads sizes the pool of CPU threads that evaluate host-assigned
- * experts (0 = all hardware threads).  A cache is not thread-safe: one
+ * experts (0 = min(16, hardware threads)).  A cache is not thread-safe: one
  * caller thread per cache.
  */
 typedef struct ecf_cache ecf_cache;
@@ -232,7 +233,8 @@ typedef struct {
  * readback (the q* decision is taken on the host from the step's miss count
  * [TF "Bandwidth-adaptive execution (q* policy)"]), computes host-assigned
  * experts on the cache's host threads, and returns with the rest queued.
- * n_tokens == 0 is a no-op.  stats (nullable) receives the step's figures.
+ * n_tokens == 0 is a no-op; n_tokens * top_k above 2^26 is ECF_EINVAL (row
+ * indices are 32-bit).  stats (nullable) receives the step's figures.
  */
 int moe_layer_forward(const ecf_layer_args *args, const void *d_x, int32_t n_tokens, float *d_out,
                       ecf_step_stats *stats);

@@ -49,6 +49,19 @@ def test_invalid_shapes_rejected():
     assert ecf.ecf_workspace_bytes(ecf.make_shape(256, 64, 4, 2), 10) > 0
 
 
+def test_token_count_bound():
+    """Row indices are 32-bit: n_tokens * top_k is capped at 2^26, in the
+    workspace query and in the forward call (rejected before any device work)."""
+    sh = ecf.make_shape(256, 64, 8, 4)
+    assert ecf.ecf_workspace_bytes(sh, (1 << 26) // 4) > 0
+    with pytest.raises(ecf.EcfError):
+        ecf.ecf_workspace_bytes(sh, (1 << 26) // 4 + 1)
+    a = ecf.LayerArgs()
+    a.shape = sh
+    rc = ecf.lib().moe_layer_forward(ctypes.byref(a), None, (1 << 26) // 4 + 1, None, None)
+    assert rc == ecf.ECF_EINVAL and b"n_tokens" in ecf.lib().ecf_last_error()
+
+
 # ---- q* -----------------------------------------------------------------------------
 
 def test_qstar_matches_oracle_golden():
