@@ -14,6 +14,8 @@
 // free slot, else the least recently used entry not used by the current
 // layer-step; entries of the current layer-step are pinned until the next
 // lookup opens a new one.
+#include <memory>
+
 #include "cache_internal.h"
 
 using ecf::set_error;
@@ -59,7 +61,7 @@ int ecf_cache_create(int32_t n_layers, int32_t n_experts, int32_t n_slots, int32
         if (!out || n_layers <= 0 || n_experts <= 0 || n_slots < 0 || max_slots < n_slots ||
             (max_slots > 0 && (!d_slots || slot_bytes == 0)) || host_threads < 0)
             return set_error(ECF_EINVAL, "ecf_cache_create: bad arguments");
-        auto *c = new ecf_cache();
+        std::unique_ptr<ecf_cache> c(new ecf_cache());  // freed if an allocation below throws
         c->L = n_layers;
         c->E = n_experts;
         c->n_slots = n_slots;
@@ -76,7 +78,7 @@ int ecf_cache_create(int32_t n_layers, int32_t n_experts, int32_t n_slots, int32
         for (int32_t s = 0; s < n_slots; ++s)
             c->free.insert(s);
         c->host_threads = host_threads;
-        *out = c;
+        *out = c.release();
         return ECF_OK;
     } catch (...) {
         return set_error(ECF_EINVAL, "ecf_cache_create: allocation failed");
