@@ -58,12 +58,24 @@ void HostPool::worker()
             fn = fn_;
             total = total_;
         }
-        for (int i = next_.fetch_add(1); i < total; i = next_.fetch_add(1))
-            (*fn)(i);
+        run_tasks(*fn, total);
         {
             std::lock_guard<std::mutex> g(mu_);
             if (--busy_ == 0)
                 done_cv_.notify_all();
+        }
+    }
+}
+
+void HostPool::run_tasks(const std::function<void(int)> &fn, int total)
+{
+    for (int i = next_.fetch_add(1); i < total; i = next_.fetch_add(1)) {
+        try {
+            fn(i);
+        } catch (...) {
+            std::lock_guard<std::mutex> g(mu_);
+            if (!err_)
+                err_ = std::current_exception();
         }
     }
 }
@@ -81,10 +93,15 @@ void HostPool::parallel_for(int n, const std::function<void(int)> &fn)
         ++epoch_;
     }
     cv_.notify_all();
-    for (int i = next_.fetch_add(1); i < n; i = next_.fetch_add(1))
-        fn(i);
+    run_tasks(fn, n);
     std::unique_lock<std::mutex> lk(mu_);
     done_cv_.wait(lk, [&] { return busy_ == 0; });
+    if (err_) {
+        std::exception_ptr e = err_;
+        err_ = nullptr;
+        lk.unlock();
+        std::rethrow_exception(e);
+    }
 }
 
 // ---- dot products ----------------------------------------------------------------

@@ -4,6 +4,7 @@
 #include <atomic>
 #include <condition_variable>
 #include <cstdint>
+#include <exception>
 #include <functional>
 #include <mutex>
 #include <thread>
@@ -20,10 +21,15 @@ public:
     explicit HostPool(int n_threads);
     ~HostPool();
     int size() const { return (int)th_.size() + 1; }
+    // fn(0..n-1) over the pool and the calling thread; returns once every call
+    // has ended.  The first exception a call throws is rethrown here, after
+    // the other calls have finished.
     void parallel_for(int n, const std::function<void(int)> &fn);
 
 private:
     void worker();
+    void run_tasks(const std::function<void(int)> &fn, int total);
+    std::exception_ptr err_;
     std::vector<std::thread> th_;
     std::mutex mu_;
     std::condition_variable cv_, done_cv_;
