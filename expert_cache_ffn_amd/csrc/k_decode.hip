@@ -116,12 +116,15 @@ __device__ __forceinline__ void fma_rows(const float (&w)[N], const float *__res
 // lanes covers 8*V elements per load and UNR loads.  MXFP4 elements are
 // expanded to fp32 by v_cvt_scalef32_pk_f32_fp4 (element 2i in the low nibble
 // of byte i; the power-of-two scale is applied exactly).
+// a 16-byte MXFP4 load feeds 4x the arithmetic of a bf16 one, so it takes
+// twice the loads in flight
 template <int WF>
+constexpr int kRowUnr = WF == WF_MX ? 8 : 4;
+
+template <int WF, int UNR_ = kRowUnr<WF>>
 struct RowRegs {
     static constexpr int V = WF == WF_MX ? 32 : WF == WF_BF16 ? 8 : 4;
-    // a 16-byte MXFP4 load feeds 4x the arithmetic of a bf16 one, so it takes
-    // twice the loads in flight
-    static constexpr int UNR = WF == WF_MX ? 8 : 4;
+    static constexpr int UNR = UNR_;
     static constexpr int SPAN = 8 * V * UNR;  // elements one group covers per batch
     uint4 wv[UNR];
     uint32_t sb[UNR];
@@ -226,6 +229,33 @@ __device__ __forceinline__ void row_dots(const void *__restrict__ wrow, const ui
 #pragma unroll
     for (int q = 0; q < kDecodeNT; ++q)
         acc[q] += (part[q][0] + part[q][1]) + (part[q][2] + part[q][3]);
+}
+
+// row_dots over RPG rows at once: each batch's loads for every row are issued
+// before any of them is used (RPG times the loads in flight), then each row
+// meets the staged activations exactly as in row_dots.
+template <int WF, int RPG>
+__device__ __forceinline__ void row_dots_multi(const char *const (&wrow)[RPG], const uint8_t *const (&srow)[RPG],
+                                               const float *__restrict__ xs, int ld, int kbeg, int kend, int sub,
+                                               int nt, float (&acc)[RPG][kDecodeNT])
+{
+    // the loads in flight per lane stay those of one row in row_dots
+    using Regs = RowRegs<WF, (kRowUnr<WF> / RPG > 0 ? kRowUnr<WF> / RPG : 1)>;
+    Regs rr[RPG];
+    float part[RPG][kDecodeNT][4] = {};
+    for (int c = kbeg + sub * Regs::V; c < kend; c += Regs::SPAN) {
+#pragma unroll
+        for (int r = 0; r < RPG; ++r)
+            rr[r].load(wrow[r], srow[r], c, kend);
+#pragma unroll
+        for (int r = 0; r < RPG; ++r)
+            rr[r].apply(xs, ld, c, kend, nt, part[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < RPG; ++r)
+#pragma unroll
+        for (int q = 0; q < kDecodeNT; ++q)
+            acc[r][q] += (part[r][q][0] + part[r][q][1]) + (part[r][q][2] + part[r][q][3]);
 }
 
 // row_dots against bf16-staged activations (bf16 or MXFP4 weights).
@@ -334,7 +364,9 @@ __global__ __launch_bounds__(256) void k_decode_down(
     const int32_t *__restrict__ n_active, const int32_t *__restrict__ offsets,
     const float *__restrict__ H, int d, int I, int E, int R, int ntp, float *__restrict__ Y)
 {
-    static_assert(OB * KP == 32, "32 groups of 8 lanes per block");
+    // 32 groups of 8 lanes; KP groups share a row; each group takes RPG rows
+    static_assert((OB * KP) % 32 == 0, "32 groups of 8 lanes per block");
+    constexpr int RPG = OB * KP / 32, OG = OB / RPG;
     extern __shared__ float hs[];  // [min(kDecodeNT, T)][xpad_len(I)]
     __shared__ float red[KP][OB][kDecodeNT];
     if ((int)blockIdx.y >= *n_active)
@@ -348,12 +380,17 @@ __global__ __launch_bounds__(256) void k_decode_down(
         return;
     const int tid = threadIdx.x, lane = tid & 63, sub = lane & 7;
     const int g = tid >> 3;
-    const int rho = g % OB, kap = g / OB;
+    const int rho = g % OG, kap = g / OG;
     const int o0 = blockIdx.x * OB;
-    const size_t orow = (size_t)(o0 + rho);
-    const char *wrow = (const char *)blob + off_down +
-                       (WF == WF_MX ? orow * I / 2 : orow * I * (WF == WF_BF16 ? 2 : 4));
-    const uint8_t *srow = (const uint8_t *)blob + off_sdown + orow * (I / 32);
+    const char *wrow[RPG];
+    const uint8_t *srow[RPG];
+#pragma unroll
+    for (int r = 0; r < RPG; ++r) {  // this group's rows rho, rho + OG, ...
+        const size_t orow = (size_t)(o0 + rho + r * OG);
+        wrow[r] = (const char *)blob + off_down +
+                  (WF == WF_MX ? orow * I / 2 : orow * I * (WF == WF_BF16 ? 2 : 4));
+        srow[r] = (const uint8_t *)blob + off_sdown + orow * (I / 32);
+    }
     const int Lk = I / KP, kbeg = kap * Lk, kend = kbeg + Lk;
     for (int tp = 0; tp < ne; tp += ntp) {
         const int nt = min(ntp, ne - tp);
@@ -363,21 +400,28 @@ __global__ __launch_bounds__(256) void k_decode_down(
                     *reinterpret_cast<const float4 *>(H + (size_t)(r0 + tp + q) * I + c);
         __syncthreads();
         {
-            float acc[kDecodeNT] = {};
-            row_dots<WF>(wrow, srow, hs, I, kbeg, kend, sub, nt, acc);
+            float acc[RPG][kDecodeNT] = {};
+            if (RPG == 1)
+                row_dots<WF>(wrow[0], srow[0], hs, I, kbeg, kend, sub, nt, acc[0]);
+            else
+                row_dots_multi<WF, RPG>(wrow, srow, hs, I, kbeg, kend, sub, nt, acc);
 #pragma unroll
-            for (int q = 0; q < kDecodeNT; ++q) {
-                acc[q] += __shfl_xor(acc[q], 1, 64);
-                acc[q] += __shfl_xor(acc[q], 2, 64);
-                acc[q] += __shfl_xor(acc[q], 4, 64);
-            }
+            for (int r = 0; r < RPG; ++r)
+#pragma unroll
+                for (int q = 0; q < kDecodeNT; ++q) {
+                    acc[r][q] += __shfl_xor(acc[r][q], 1, 64);
+                    acc[r][q] += __shfl_xor(acc[r][q], 2, 64);
+                    acc[r][q] += __shfl_xor(acc[r][q], 4, 64);
+                }
             if (sub == 0)
 #pragma unroll
-                for (int q = 0; q < kDecodeNT; ++q)
-                    red[kap][rho][q] = acc[q];
+                for (int r = 0; r < RPG; ++r)
+#pragma unroll
+                    for (int q = 0; q < kDecodeNT; ++q)
+                        red[kap][rho + r * OG][q] = acc[r][q];
             __syncthreads();
-            if (tid < OB * nt) {
-                const int ol = tid % OB, q = tid / OB;
+            for (int i = tid; i < OB * nt; i += 256) {
+                const int ol = i % OB, q = i / OB;
                 float sum = 0.f;
 #pragma unroll
                 for (int p = 0; p < KP; ++p)
@@ -488,21 +532,27 @@ int launch_decode_down(const ecf_shape &s, const ExpertTables &ex, const RouteOu
 {
     const int R = T * s.top_k;
     const int maxa = std::min(s.n_experts, R);
-    constexpr int OB = 32, KP = 1;
-    dim3 grid(s.hidden / OB, maxa);
+    constexpr int KP = 1;
     const int ntp = std::min(kDecodeNT, T);
     const size_t sh = sizeof(float) * ntp * xpad_len(s.inter);
     ProfScope p("decode_down", st);
-#define ECF_DN(WFV)                                                                                 \
-    hipLaunchKernelGGL((k_decode_down<WFV, OB, KP>), grid, dim3(256), sh, st, ex.ptrs, ex.lay.off[2],  \
-                       ex.lay.off[5], o.active, o.n_active, o.offsets, H, s.hidden, s.inter,          \
-                       s.n_experts, R, ntp, Y)
-    if (s.w_dtype == ECF_MXFP4)
-        ECF_DN(WF_MX);
+#define ECF_DN(WFV, OBV)                                                                            \
+    hipLaunchKernelGGL((k_decode_down<WFV, OBV, KP>), dim3(s.hidden / (OBV), maxa), dim3(256), sh, st, \
+                       ex.ptrs, ex.lay.off[2], ex.lay.off[5], o.active, o.n_active, o.offsets, H,     \
+                       s.hidden, s.inter, s.n_experts, R, ntp, Y)
+    // MXFP4 rows are a quarter of a bf16 row, so a 32-row block reads only 17 KB
+    // after its fixed chain of latencies (routing tables, h staging, barrier);
+    // with 64 or more routed rows 128-row blocks (each group's 4 rows loaded
+    // together) still fill the GPU: d 4096, I 1024, 16 tokens 53.6 -> 50.0 us.
+    // Below that (e.g. 6 rows at one token) there are too few of them.
+    if (s.w_dtype == ECF_MXFP4 && R >= 64)
+        ECF_DN(WF_MX, 128);
+    else if (s.w_dtype == ECF_MXFP4)
+        ECF_DN(WF_MX, 32);
     else if (s.w_dtype == ECF_BF16)
-        ECF_DN(WF_BF16);
+        ECF_DN(WF_BF16, 32);
     else
-        ECF_DN(WF_F32);
+        ECF_DN(WF_F32, 32);
 #undef ECF_DN
     ECF_HIP_CHECK(hipGetLastError());
     return ECF_OK;
