@@ -182,6 +182,13 @@ __attribute__((target("avx2,fma"))) inline __m256 e2m1x8(__m256i code, __m256 sc
 }
 
 // Same sums with AVX2: two 8-wide accumulators per row = 16 partial sums.
+// Byte offset of element c within a weight row.
+template <int WF>
+constexpr size_t wbytes(int c)
+{
+    return WF == HF_MX ? (size_t)c / 2 : (size_t)c * (WF == HF_BF16 ? 2 : 4);
+}
+
 template <int WF>
 __attribute__((target("avx2,fma"))) void dots_avx2(const void *w, const uint8_t *sc, const float *const *xs,
                                                    int nr, int n, float *out)
@@ -193,6 +200,7 @@ __attribute__((target("avx2,fma"))) void dots_avx2(const void *w, const uint8_t 
         for (int r = 0; r < kRowsPerDot; ++r)
             acc[r][0] = acc[r][1] = _mm256_setzero_ps();
         for (int c = 0; c < n; c += STEP) {
+            _mm_prefetch((const char *)w + wbytes<WF>(c) + 1024, _MM_HINT_T0);  // 1 KB ahead
             __m256 wv[4];
             if (WF == HF_MX) {
                 const __m128i bytes = _mm_loadu_si128((const __m128i *)((const uint8_t *)w + c / 2));
@@ -245,6 +253,9 @@ __attribute__((target("avx512f,avx512bw,avx512vl,avx512bf16"))) void dots_avx512
         for (int r = 0; r < kRowsPerDot; ++r)
             acc[r][0] = acc[r][1] = _mm512_setzero_ps();
         for (int c = 0; c < n; c += 32) {  // n is a multiple of 32
+            // the weight stream 1 KB ahead (past a row's end it touches the next row;
+            // a prefetch never faults)
+            _mm_prefetch((const char *)w + wbytes<WF>(c) + 1024, _MM_HINT_T0);
             if (dp) {
                 const __m512i wv = _mm512_loadu_si512((const void *)((const uint16_t *)w + c));
                 for (int r = 0; r < m; ++r) {
@@ -364,22 +375,36 @@ int host_experts(HostPool &pool, const ecf_shape &s, const BlobLayout &lay,
         hoff[j + 1] = hoff[j] + jobs[j].rows.size() * (size_t)I;
     std::vector<float> h(hoff.back());
 
-    constexpr int CH = 16;  // weight rows per task
-    const int gu_chunks = (I + CH - 1) / CH, dn_chunks = (d + CH - 1) / CH;
+    // weight rows per task: 16 gate + 16 up rows (256 KB of bf16 at d 4096), 64
+    // down rows (128 KB at I 1024), so a task's fixed costs stay small
+    constexpr int CH = 16, CHD = 64;
+    const int gu_chunks = (I + CH - 1) / CH, dn_chunks = (d + CHD - 1) / CHD;
     const int nj = (int)jobs.size();
+    // per-thread scratch, reused across tasks and calls (the pool's threads persist)
+    struct Scratch {
+        std::vector<const float *> xs;
+        std::vector<const uint16_t *> xb;
+        std::vector<float> a, b;
+    };
+    static thread_local Scratch tls;
 
     pool.parallel_for(nj * gu_chunks, [&](int task) {
         const HostExpertJob &jb = jobs[task / gu_chunks];
         const int nr = (int)jb.rows.size();
-        std::vector<const float *> xs(nr);
-        std::vector<const uint16_t *> xb(nr);
+        Scratch &sc = tls;
+        sc.xs.resize(nr);
+        sc.xb.resize(nr);
+        sc.a.resize(nr);
+        sc.b.resize(nr);
+        std::vector<const float *> &xs = sc.xs;
+        std::vector<const uint16_t *> &xb = sc.xb;
         for (int r = 0; r < nr; ++r) {
             const size_t t = (size_t)(jb.rows[r] / k);
             xs[r] = xf.data() + t * d;
             xb[r] = xbf ? (const uint16_t *)x + t * d : nullptr;
         }
         const uint16_t *const *xbp = xbf ? xb.data() : nullptr;
-        std::vector<float> a(nr), b(nr);
+        std::vector<float> &a = sc.a, &b = sc.b;
         float *hj = h.data() + hoff[task / gu_chunks];
         const int i0 = (task % gu_chunks) * CH, i1 = std::min(I, i0 + CH);
         for (int i = i0; i < i1; ++i) {
@@ -394,11 +419,14 @@ int host_experts(HostPool &pool, const ecf_shape &s, const BlobLayout &lay,
         const HostExpertJob &jb = jobs[task / dn_chunks];
         const int nr = (int)jb.rows.size();
         const float *hj = h.data() + hoff[task / dn_chunks];
-        std::vector<const float *> hs(nr);
+        Scratch &sc = tls;
+        sc.xs.resize(nr);
+        sc.a.resize(nr);
+        std::vector<const float *> &hs = sc.xs;
         for (int r = 0; r < nr; ++r)
             hs[r] = hj + (size_t)r * I;
-        std::vector<float> o(nr);
-        const int o0 = (task % dn_chunks) * CH, o1 = std::min(d, o0 + CH);
+        std::vector<float> &o = sc.a;
+        const int o0 = (task % dn_chunks) * CHD, o1 = std::min(d, o0 + CHD);
         for (int oo = o0; oo < o1; ++oo) {
             dots_any(isa, wf, row_of(jb.blob, lay.off[2], lay.off[5], wf, oo, I), hs.data(), nullptr, nr, I,
                      o.data());
