@@ -52,7 +52,7 @@ constexpr int kSortSeg = 1024;      // rows per segment of the multi-block count
 constexpr int kSmallRouteRows = 2048; // R up to this uses the single-block routing kernel
 constexpr int kPrefillMT = 128;     // rows per prefill GEMM tile (bf16 weights)
 #ifndef ECF_MX_BM
-#define ECF_MX_BM 256                // rows per prefill GEMM tile (MXFP4 weights)
+#define ECF_MX_BM 320                // rows per prefill GEMM tile (MXFP4 weights)
 #endif
 constexpr int kDecodeNT = 2;        // max rows per pass of the decode GEMV kernels
 

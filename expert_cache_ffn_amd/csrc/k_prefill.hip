@@ -4,7 +4,7 @@
 // In prefill thousands of tokens reach nearly every expert of a layer
 // (FreeToken paper explainer, section "Wall 1: prefill" -- sparsity vanishes),
 // so each expert is a small dense GEMM: its rows are contiguous in the
-// counting-sort order and tiled BM rows at a time (128 for bf16 weights, 256
+// counting-sort order and tiled BM rows at a time (128 for bf16 weights, 320
 // for MXFP4; the tile list comes from the routing kernels).
 //
 //   GEMM1: [a | b] = X_perm . [W_gate ; W_up]^T, h = silu(a) * b -> H (bf16)
@@ -14,8 +14,8 @@
 //   GEMM2: Y = H . W_down^T (fp32), combined per token by k_combine.
 //
 // Block = NW waves as WM x (NW / WM), tile BM rows x BNT weight rows, BK = 64
-// (bf16: 4 waves on 128 x 128, each 64 x 64; MXFP4: 8 waves on 256 x 256, each
-// 128 rows x 64 weight rows, i.e. 4 x 2 MFMA 32x32 fragments).  Software pipeline of depth 2 through
+// (bf16: 4 waves on 128 x 128, each 64 x 64; MXFP4: 8 waves on 320 x 256, each
+// 160 rows x 64 weight rows, i.e. up to 5 x 2 MFMA 32x32 fragments).  Software pipeline of depth 2 through
 // registers: in program order the loads of k-tile kt+2 come before the MFMAs
 // of k-tile kt and the LDS stores of k-tile kt+1 after them (the compiler's
 // schedule of that order measured faster than pinning it with scheduling
@@ -368,16 +368,20 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_grouped_gemm(
     // MFMA row blocks of this wave that hold real rows (uniform over the wave)
     // (with WM = 1 a block of 65..96 rows runs 4 row blocks: one wasted, one fewer instance)
     const int nms = __builtin_amdgcn_readfirstlane(max(0, min(NMSMAX, (mrows - wm * WROWS + 31) / 32)));
-    if constexpr (NMSMAX >= 4) {
-        if (nms >= 4) {
+    static_assert(NMSMAX <= 5, "row-block instances below cover up to 5");
+    if constexpr (NMSMAX >= 5) {
+        if (nms >= 5) {
             run(IC<NMSMAX>{});
             return;
         }
-        if (nms == 3) {
-            run(IC<3>{});
+    }
+    if constexpr (NMSMAX >= 4) {
+        if (nms == 4) {
+            run(IC<4>{});
             return;
         }
-    } else if constexpr (NMSMAX == 3) {
+    }
+    if constexpr (NMSMAX >= 3) {
         if (nms == 3) {
             run(IC<3>{});
             return;
@@ -395,10 +399,13 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_grouped_gemm(
 
 // Tile choice per weight format, measured on MI355X (bf16: 4096-token layer,
 // d 4096, I 1024, top-6; MXFP4: 8192-token layer, I 2048, top-8).  bf16 (HBM-
-// bound): 128 x 128 tiles, 4 waves as 2 x 2, two blocks per CU.  MXFP4: 256 x
-// 256 tiles, 8 waves as 2 x 4 (128 rows x 64 weight rows each), one block per
-// CU -- each expanded B fragment feeds four MFMAs and the weights stream once
-// per 256 rows; GEMM1 5% faster than 128 x 256 tiles with 4 waves.  Two-sub-tile
+// bound): 128 x 128 tiles, 4 waves as 2 x 2, two blocks per CU.  MXFP4: 320 x
+// 256 tiles, 8 waves as 2 x 4 (160 rows x 64 weight rows each), one block per
+// CU -- each expanded B fragment feeds up to five MFMAs, and an expert with up
+// to 320 rows streams its weights through one tile: with ~256 +- 16 rows per
+// expert, 256-row tiles left a tail tile (a whole weight pass for a few dozen
+// rows) on half the experts; 320-row tiles took the layer from 3.94 to 3.64 ms
+// (256-row tiles with 8 waves were 5% faster than 4 waves on 128 x 256).  Two-sub-tile
 // stages, a 1 x 4 wave layout, three blocks per CU, expanding MXFP4 to bf16 once
 // at the LDS store, 4 waves on 256 x 256 and 8 waves on 128 x 256 were each
 // slower or spilled registers.

@@ -173,9 +173,11 @@ def test_prefill_bf16_full_size_sampled():
 
 # ---- prefill MXFP4 ------------------------------------------------------------------------
 
-# 256-row tiles: 600 x 2 over 4 experts gives each expert a full tile and a
-# 44-row tail (every wave-row count 0..4); 1200 x 2 also takes the multi-block sort
-@pytest.mark.parametrize("T,E,k,I", [(260, 8, 2, 256), (64, 4, 4, 128), (600, 4, 2, 256), (1200, 4, 2, 128)])
+# 320-row tiles (two waves of 160 rows): 600 x 2 over 4 experts is one 300-row
+# tile per expert, 800 x 2 a full tile and an 80-row tail (row blocks per wave
+# 0..5), 1200 x 2 a full tile and a 280-row one and takes the multi-block sort
+@pytest.mark.parametrize("T,E,k,I", [(260, 8, 2, 256), (64, 4, 4, 128), (600, 4, 2, 256), (800, 4, 2, 256),
+                                     (1200, 4, 2, 128)])
 def test_prefill_mxfp4_small(T, E, k, I):
     cfg = cfg_small(experts=E, top_k=k, inter=I, w_dtype="mxfp4", logits="normal_t", temperature=0.5,
                     cid=80 + E)
