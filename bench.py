@@ -303,7 +303,41 @@ def cpu_baseline_decode(torch, syn, sample, budget_s=15.0, T=16, max_batches=256
 
 # ---- prefill (bf16 and MXFP4) ----------------------------------------------------------------
 
-def bench_prefill(torch, ecf, syn, name, steps, warmup):
+def cpu_oracle_prefill(torch, syn, cfg, x, lg, counts_gpu, out_gpu, sample=128):
+    """The oracle on a bounded sample of a prefill layer: routing, counts and
+    permutation of all T tokens, the expert FFNs and combine of the first
+    `sample` tokens (every expert they reach), timed; those tokens' GPU outputs
+    and the layer's expert counts are checked against it."""
+    import numpy as np
+    import oracle
+    T, E, k = cfg.tokens[0], cfg.experts, cfg.top_k
+    toks = np.arange(min(sample, T))
+    lg_c, x_c = lg.float().cpu(), x.cpu()
+    idx, _ = oracle.route(lg_c, k)
+    need = sorted(set(int(v) for v in idx[toks].ravel()))
+    experts = [None] * E
+    for e in need:  # the same seeded tensors the GPU blobs were packed from
+        experts[e] = {n: t.detach().cpu() for n, t in syn.expert_weights(cfg, 0, e, device="cuda").items()}
+    t0 = time.perf_counter()
+    res = oracle.moe_layer(x_c, experts, k, lg=lg_c, w_dtype=cfg.w_dtype, tokens=toks)
+    el = time.perf_counter() - t0
+    tol = 5e-2 if cfg.w_dtype == "mxfp4" else 2e-2
+    got = out_gpu[: len(toks)].cpu().numpy()
+    rms = float(np.sqrt(np.mean(res["out"] ** 2)))
+    err = float(np.max(np.abs(got - res["out"]))) / rms
+    counts_ok = bool(np.array_equal(counts_gpu.cpu().numpy(), res["counts"]))
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    r = {"value": len(toks) / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+         "sample": f"routing of all {T} tokens and the experts of the first {len(toks)} ({len(need)} experts), "
+                   f"{el:.1f} s of CPU time",
+         "checked_against_gpu": {"tokens": int(len(toks)), "counts_exact": counts_ok, "max_err_over_rms": err,
+                                 "tolerance": tol, "ok": bool(counts_ok and err <= tol)}}
+    log(f"{cfg.name}: oracle {r['value']:.1f} tok/s on {threads} threads ({r['sample']}); GPU counts "
+        f"{'exact' if counts_ok else 'DIFFER'}, max|err|/RMS {err:.2e} on {len(toks)} tokens")
+    return r
+
+
+def bench_prefill(torch, ecf, syn, name, steps, warmup, cpu=False):
     from expert_cache_ffn_amd.layer import ExpertPool, Layer
     cfg = syn.CONFIGS[name]
     T, d, E, I, k = cfg.tokens[0], cfg.hidden, cfg.experts, cfg.inter, cfg.top_k
@@ -361,6 +395,12 @@ def bench_prefill(torch, ecf, syn, name, steps, warmup):
     if g1 and g2:
         res["gemm1_tflops"] = 2.0 * R * d * 2 * I / (g1 * 1e-6) / 1e12
         res["gemm2_tflops"] = 2.0 * R * I * d / (g2 * 1e-6) / 1e12
+    if cpu:  # the oracle beside it, on batch 0 (what `counts` holds)
+        lay.forward(lay.args(router_logits=lgs[0], expert_ptrs=pool.ptrs), xs[0], out, False)
+        torch.cuda.synchronize()
+        # MXFP4 expert FFNs take the oracle ~0.15 s per token: a smaller sample
+        res["cpu_oracle"] = cpu_oracle_prefill(torch, syn, cfg, xs[0], lgs[0], counts, out,
+                                               sample=32 if cfg.w_dtype == "mxfp4" else 128)
     log(f"{name}: {ms:.3f} ms/layer (median {per_step[steps // 2]:.3f}), {res['tokens_per_s']:.0f} tok/s, "
         f"{res['tflops']:.0f} TFLOP/s "
         f"({100 * res['mfma_frac']:.1f}% MFMA), weights {res['weight_GBps']:.0f} GB/s")
@@ -650,10 +690,10 @@ def main():
         torch.cuda.empty_cache()
     if "prefill" in wl:
         also["prefill_bf16_T4096"] = bench_prefill(torch, ecf, syn, "prefill", max(20, args.steps // 10),
-                                                   max(2, args.warmup // 5))
+                                                   max(2, args.warmup // 5), cpu=not args.no_cpu_baseline)
     if "prefill_fp4" in wl:
         also["prefill_mxfp4_T8192"] = bench_prefill(torch, ecf, syn, "prefill_fp4", max(20, args.steps // 10),
-                                                    max(2, args.warmup // 5))
+                                                    max(2, args.warmup // 5), cpu=not args.no_cpu_baseline)
     if sample is not None and not args.no_cpu_baseline:
         log("cpu baseline: oracle on sampled decode batches")
         cpu = cpu_baseline_decode(torch, syn, sample)
