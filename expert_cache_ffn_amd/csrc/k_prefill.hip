@@ -14,7 +14,7 @@
 //   GEMM2: Y = H . W_down^T (fp32), combined per token by k_combine.
 //
 // Block = NW waves as WM x (NW / WM), tile BM rows x BNT weight rows, BK = 64
-// (bf16: 4 waves on 128 x 128, each 64 x 64; MXFP4: 8 waves on 320 x 256, each
+// (bf16: 8 waves on 128 x 256, each 64 x 64; MXFP4: 8 waves on 320 x 256, each
 // 160 rows x 64 weight rows, i.e. up to 5 x 2 MFMA 32x32 fragments).  Software pipeline of depth 2 through
 // registers: in program order the loads of k-tile kt+2 come before the MFMAs
 // of k-tile kt and the LDS stores of k-tile kt+1 after them (the compiler's
@@ -399,7 +399,9 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_grouped_gemm(
 
 // Tile choice per weight format, measured on MI355X (bf16: 4096-token layer,
 // d 4096, I 1024, top-6; MXFP4: 8192-token layer, I 2048, top-8).  bf16 (HBM-
-// bound): 128 x 128 tiles, 4 waves as 2 x 2, two blocks per CU.  MXFP4: 320 x
+// bound): 128 x 256 tiles, 8 waves as 2 x 4 (64 x 64 each), one block per CU --
+// half the A re-reads of 128 x 128 tiles with 4 waves (layer 1.48 -> 1.41 ms).
+// MXFP4: 320 x
 // 256 tiles, 8 waves as 2 x 4 (160 rows x 64 weight rows each), one block per
 // CU -- each expanded B fragment feeds up to five MFMAs, and an expert with up
 // to 320 rows streams its weights through one tile: with ~256 +- 16 rows per
@@ -410,13 +412,13 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_grouped_gemm(
 // at the LDS store, 4 waves on 256 x 256 and 8 waves on 128 x 256 were each
 // slower or spilled registers.
 #ifndef ECF_BF16_BNT
-#define ECF_BF16_BNT 128
-#define ECF_BF16_MINB 2
+#define ECF_BF16_BNT 256
+#define ECF_BF16_MINB 1
 #define ECF_BF16_KS 1
 #define ECF_BF16_WM 2
 #endif
 #ifndef ECF_BF16_NW
-#define ECF_BF16_NW 4
+#define ECF_BF16_NW 8
 #endif
 #ifndef ECF_MX_BNT
 #define ECF_MX_BNT 256
