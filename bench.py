@@ -14,7 +14,8 @@ prefill (8192 tokens, I 2048, top-8), the 43-layer cached decode with 37% slots
 and the q* split, the machine's B_P / B_H from ecf_bandwidth_profile, the
 cached-decode policy ablation at equal capacity (q* at the configured and at the
 measured ratio, every miss over PCIe, a static hot subset with every miss on the
-host), and the prefill layer prefetch overlap.  `roofline` is for the
+host), the prefill layer prefetch overlap, and torch.bmm on the prefill
+GEMM shapes (a vendor-library calibration).  `roofline` is for the
 dominant kernel of the headline workload (decode gate/up GEMV); `cpu_baseline`
 is the oracle on a bounded sample of the headline workload.
 
@@ -79,6 +80,41 @@ def bench_hbm(torch, ecf, reps=10):
     out["peak_GBps"] = HBM_PEAK_GBS
     log(f"hbm: plain read {out['read_GBps']:.0f} GB/s, device copy {out['copy_GBps']:.0f} GB/s "
         f"(read+write), datasheet peak {HBM_PEAK_GBS:.0f}")
+    return out
+
+
+def bench_vendor_gemm(torch, reps=5):
+    """Calibration, not part of the layer: torch.bmm (the ROCm BLAS libraries)
+    on the prefill layers' per-expert GEMM shapes with every expert holding
+    exactly R/E rows and dense bf16 weights (no ragged tiles, no MXFP4
+    expansion), plus one large square GEMM -- what the vendor's GEMMs reach on
+    this GPU for the same work.  Right operands are contiguous [E, K, N]."""
+    shapes = {  # name: (batch, M, K, N)
+        "square_8192": (1, 8192, 8192, 8192),
+        "prefill_bf16_gemm1": (256, 96, 4096, 2048),    # 4096 tokens x top-6 / 256 experts; [gate|up]
+        "prefill_bf16_gemm2": (256, 96, 1024, 4096),
+        "prefill_mxfp4_gemm1": (256, 256, 4096, 4096),  # 8192 tokens x top-8 / 256 experts
+        "prefill_mxfp4_gemm2": (256, 256, 2048, 4096),
+    }
+    out = {}
+    for name, (bt, m, kk, n) in shapes.items():
+        a = torch.randn(bt, m, kk, device="cuda", dtype=torch.bfloat16)
+        b = torch.randn(bt, kk, n, device="cuda", dtype=torch.bfloat16)
+        c = torch.bmm(a, b)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(reps):
+            torch.bmm(a, b, out=c)
+        ev1.record()
+        torch.cuda.synchronize()
+        us = 1e3 * ev0.elapsed_time(ev1) / reps
+        tf = 2.0 * bt * m * kk * n / (us * 1e-6) / 1e12
+        out[name] = {"batch": bt, "M": m, "K": kk, "N": n, "us": us, "tflops": tf,
+                     "mfma_frac": tf / BF16_PEAK_TFLOPS}
+        del a, b, c
+    torch.cuda.empty_cache()
+    log("vendor bmm: " + ", ".join(f"{k} {v['us']:.0f} us ({v['tflops']:.0f} TF)" for k, v in out.items()))
     return out
 
 
@@ -638,10 +674,11 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workloads",
-                    default="hbm,decode,decode_fp4,prefill,prefill_fp4,prefetch,cached,bandwidth,policies,cached_fp4",
-                    help="any of hbm, decode, decode_fp4, prefill, prefill_fp4, prefetch, cached, bandwidth, policies, "
-                         "cached_fp4 (policies: the cached-decode policy ablation at equal capacity; *_fp4: the "
-                         "same layers with MXFP4 experts)")
+                    default="hbm,decode,decode_fp4,prefill,prefill_fp4,vendor,prefetch,cached,bandwidth,policies,"
+                            "cached_fp4",
+                    help="any of hbm, decode, decode_fp4, prefill, prefill_fp4, vendor, prefetch, cached, bandwidth, "
+                         "policies, cached_fp4 (policies: the cached-decode policy ablation at equal capacity; *_fp4: "
+                         "the same layers with MXFP4 experts; vendor: torch.bmm on the prefill GEMM shapes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--cached-steps", type=int, default=12)
@@ -694,6 +731,8 @@ def main():
     if "prefill_fp4" in wl:
         also["prefill_mxfp4_T8192"] = bench_prefill(torch, ecf, syn, "prefill_fp4", max(20, args.steps // 10),
                                                     max(2, args.warmup // 5), cpu=not args.no_cpu_baseline)
+    if "vendor" in wl:
+        also["vendor_bmm_calibration"] = bench_vendor_gemm(torch)
     if sample is not None and not args.no_cpu_baseline:
         log("cpu baseline: oracle on sampled decode batches")
         cpu = cpu_baseline_decode(torch, syn, sample)
