@@ -548,8 +548,8 @@ int launch_decode_gateup(const ecf_shape &s, const ExpertTables &ex, const Route
     const size_t sh = dot2 ? sizeof(uint16_t) * ntp * xpadh_len(s.hidden) : sizeof(float) * ntp * xpad_len(s.hidden);
     ProfScope p("decode_gateup", st);
     const bool abf = s.a_dtype == ECF_BF16;
-#define ECF_GU(WFV, AB, IBV)                                                                        \
-    hipLaunchKernelGGL((k_decode_gateup<WFV, AB, IBV, KP>), dim3(s.inter / (IBV), maxa), dim3(256), sh, st, \
+#define ECF_GU(WFV, AB, IBV, KPV)                                                                   \
+    hipLaunchKernelGGL((k_decode_gateup<WFV, AB, IBV, KPV>), dim3(s.inter / (IBV), maxa), dim3(256), sh, st, \
                        ex.ptrs, ex.lay.off[0], ex.lay.off[1], ex.lay.off[3], ex.lay.off[4], o.active,   \
                        o.n_active, o.offsets, o.perm, x, s.hidden, s.inter, s.top_k, s.n_experts, R,  \
                        ntp, H)
@@ -557,16 +557,21 @@ int launch_decode_gateup(const ecf_shape &s, const ExpertTables &ex, const Route
     // rows, 16-row blocks whose groups load gate row i and up row i together
     // (d 4096, I 1024, 16 tokens: 74.0 -> 71.3 us); at one token (6 rows) the
     // 8-row blocks are faster (14.0 against 15.0 us).
+    // bf16: 2-row blocks (gate row i and up row i) with each row split over 8
+    // groups (1 KB each), so every expert spreads over 8x more blocks than
+    // 8-row blocks in 2 parts: d 4096, I 1024, gate/up 223 -> 197 us at 16
+    // tokens, 71 -> 60 us at 4, 24 -> 21 us at 1 (MXFP4 got slower split this
+    // way: its rows are a quarter as long and its arithmetic per byte 4x).
     if (s.w_dtype == ECF_MXFP4 && R >= 64)
-        ECF_GU(WF_MX, true, 16);
+        ECF_GU(WF_MX, true, 16, KP);
     else if (s.w_dtype == ECF_MXFP4)
-        ECF_GU(WF_MX, true, 8);
+        ECF_GU(WF_MX, true, 8, KP);
     else if (s.w_dtype == ECF_BF16)
-        ECF_GU(WF_BF16, true, 8);
+        ECF_GU(WF_BF16, true, 2, 8);
     else if (abf)
-        ECF_GU(WF_F32, true, 8);
+        ECF_GU(WF_F32, true, 8, KP);
     else
-        ECF_GU(WF_F32, false, 8);
+        ECF_GU(WF_F32, false, 8, KP);
 #undef ECF_GU
     ECF_HIP_CHECK(hipGetLastError());
     return ECF_OK;
@@ -581,8 +586,8 @@ int launch_decode_down(const ecf_shape &s, const ExpertTables &ex, const RouteOu
     const int ntp = std::min(kDecodeNT, T);
     const size_t sh = sizeof(float) * ntp * xpad_len(s.inter);
     ProfScope p("decode_down", st);
-#define ECF_DN(WFV, OBV)                                                                            \
-    hipLaunchKernelGGL((k_decode_down<WFV, OBV, KP>), dim3(s.hidden / (OBV), maxa), dim3(256), sh, st, \
+#define ECF_DN(WFV, OBV, KPV)                                                                       \
+    hipLaunchKernelGGL((k_decode_down<WFV, OBV, KPV>), dim3(s.hidden / (OBV), maxa), dim3(256), sh, st, \
                        ex.ptrs, ex.lay.off[2], ex.lay.off[5], o.active, o.n_active, o.offsets, H,     \
                        s.hidden, s.inter, s.n_experts, R, ntp, Y)
     // MXFP4 rows are a quarter of a bf16 row, so a 32-row block reads only 17 KB
@@ -590,14 +595,16 @@ int launch_decode_down(const ecf_shape &s, const ExpertTables &ex, const RouteOu
     // with 64 or more routed rows 128-row blocks (each group's 4 rows loaded
     // together) still fill the GPU: d 4096, I 1024, 16 tokens 53.6 -> 50.0 us.
     // Below that (e.g. 6 rows at one token) there are too few of them.
+    // bf16: 16-row blocks, each row split over 4 groups (512 B each), each group
+    // two rows: down 107 -> 103 us at 16 tokens, 35 -> 34 us at 4.
     if (s.w_dtype == ECF_MXFP4 && R >= 64)
-        ECF_DN(WF_MX, 128);
+        ECF_DN(WF_MX, 128, KP);
     else if (s.w_dtype == ECF_MXFP4)
-        ECF_DN(WF_MX, 32);
+        ECF_DN(WF_MX, 32, KP);
     else if (s.w_dtype == ECF_BF16)
-        ECF_DN(WF_BF16, 32);
+        ECF_DN(WF_BF16, 16, 4);
     else
-        ECF_DN(WF_F32, 32);
+        ECF_DN(WF_F32, 32, KP);
 #undef ECF_DN
     ECF_HIP_CHECK(hipGetLastError());
     return ECF_OK;
