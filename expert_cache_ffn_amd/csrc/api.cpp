@@ -82,7 +82,12 @@ ProfScope::ProfScope(const char *name, hipStream_t s) : name_(name), s_(s)
 {
     if (!g_prof_on)
         return;
-    if (hipEventCreate(&a_) != hipSuccess || hipEventCreate(&b_) != hipSuccess) {
+    if (hipEventCreate(&a_) != hipSuccess) {
+        a_ = nullptr;
+        return;
+    }
+    if (hipEventCreate(&b_) != hipSuccess) {
+        (void)hipEventDestroy(a_);
         a_ = b_ = nullptr;
         return;
     }
@@ -278,7 +283,7 @@ int ecf_host_experts(const ecf_shape *shape, int32_t n_jobs, const void *const *
         int rc = check_shape(shape);
         if (rc != ECF_OK)
             return rc;
-        if (n_jobs < 0 || n_tokens < 0 || n_threads < 0 ||
+        if (n_jobs < 0 || n_tokens < 0 || n_threads < 0 || (int64_t)n_tokens * shape->top_k > kMaxRows ||
             (n_jobs > 0 && (!h_blobs || !n_rows || !rows || !h_x || !h_y)))
             return set_error(ECF_EINVAL, "ecf_host_experts: bad arguments");
         BlobLayout lay;

@@ -247,7 +247,8 @@ int moe_layer_forward(const ecf_layer_args *args, const void *d_x, int32_t n_tok
  * straight from host memory].  h_blobs[i] is the host blob of job i (fp32, bf16
  * or MXFP4 weights), rows of job i are rows[sum(n_rows[<i]) .. + n_rows[i]];
  * h_x [T][d] in a_dtype, h_y [T*k][d] fp32 (only listed rows written).  No
- * GPU is touched.
+ * GPU is touched.  ECF_EINVAL for negative counts, a row outside [0, T*k),
+ * NULL arrays with n_jobs > 0, or n_tokens * top_k above 2^26.
  */
 int ecf_host_experts(const ecf_shape *shape, int32_t n_jobs, const void *const *h_blobs,
                      const int32_t *n_rows, const int32_t *rows, const void *h_x, int32_t n_tokens,

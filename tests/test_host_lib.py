@@ -60,6 +60,9 @@ def test_token_count_bound():
     a.shape = sh
     rc = ecf.lib().moe_layer_forward(ctypes.byref(a), None, (1 << 26) // 4 + 1, None, None)
     assert rc == ecf.ECF_EINVAL and b"n_tokens" in ecf.lib().ecf_last_error()
+    # the host half alone: the same cap, checked before any row is read
+    with pytest.raises(ecf.EcfError):
+        ecf.ecf_host_experts(sh, [], [], 0, (1 << 26) // 4 + 1, 0, 1)
 
 
 # ---- q* -----------------------------------------------------------------------------
