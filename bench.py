@@ -595,7 +595,7 @@ def bench_cached(torch, ecf, syn, ctx, policy="lru_qstar", bw=None):
         torch.cuda.synchronize()
     elif policy != "lru_qstar":
         raise ValueError(policy)
-    totals = dict(unique=0, hits=0, misses=0, q=0, host=0, h2d=0, hostb=0, wait=0.0, hostms=0.0)
+    totals = dict(unique=0, hits=0, gpu_experts=0, misses=0, q=0, host=0, h2d=0, hostb=0, wait=0.0, hostms=0.0)
     qhist = {}
     res_f, act, xa = ctx["res_f"], ctx["act"], ctx["xa"]
 
@@ -610,6 +610,7 @@ def bench_cached(torch, ecf, syn, ctx, policy="lru_qstar", bw=None):
             if record:
                 totals["unique"] += st["n_unique"]
                 totals["hits"] += st["hits"]
+                totals["gpu_experts"] += st["n_unique"] - st["host"]
                 totals["misses"] += st["misses"]
                 totals["q"] += st["q"]
                 totals["host"] += st["host"]
@@ -640,12 +641,14 @@ def bench_cached(torch, ecf, syn, ctx, policy="lru_qstar", bw=None):
                miss_rate_warmup=miss_cold, unique_per_layer=totals["unique"] / (steps * L),
                q_total=totals["q"], host_total=totals["host"],
                pcie_GBps=totals["h2d"] / el / 1e9, host_read_GBps=totals["hostb"] / el / 1e9,
+               # expert weights the GPU kernels read from slots (hits and copied misses)
+               hbm_expert_GBps=totals["gpu_experts"] * S / el / 1e9,
                ms_wait_route_per_step=totals["wait"] / steps, ms_host_ffn_per_step=totals["hostms"] / steps,
                q_hist={str(q): n for q, n in sorted(qhist.items())}, host_blobs=ctx["n_blobs"],
                host_threads="default (min(16, hardware threads))")
     log(f"cached {ctx['w_dtype']} [{policy}]: {res['ms_per_step']:.1f} ms/step ({L} layers), {res['tokens_per_s']:.1f} tok/s, "
         f"steady miss rate {100 * miss_steady:.1f}%, PCIe {res['pcie_GBps']:.1f} GB/s, "
-        f"host {res['host_read_GBps']:.1f} GB/s")
+        f"host {res['host_read_GBps']:.1f} GB/s, HBM (expert weights) {res['hbm_expert_GBps']:.1f} GB/s")
     return res
 
 
