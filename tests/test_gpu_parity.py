@@ -144,6 +144,25 @@ def test_residual_added():
     assert np.allclose(res["out"], base["out"] + r.cpu().numpy(), rtol=0, atol=1e-6)
 
 
+# ---- one token ------------------------------------------------------------------------
+
+@pytest.mark.parametrize("w,E,k,I", [("bf16", 16, 8, 512), ("bf16", 12, 3, 1536), ("f32", 8, 4, 512),
+                                     ("bf16", 16, 9, 512)])
+def test_one_token(w, E, k, I):
+    """T = 1 (each routed row its own expert) against the oracle, and the
+    residual added exactly: out = residual + combine in fp32."""
+    cfg = cfg_small(experts=E, top_k=k, inter=I, w_dtype=w, a_dtype="f32" if w == "f32" else "bf16",
+                    cid=90 + E + k)
+    say(f"case: one token {w} E={E} k={k} I={I}")
+    c = Case(cfg, 1)
+    base = c.run()
+    assert base["stats"]["path"] == ecf.ECF_PATH_DECODE
+    compare(base, c.oracle(), TOL[w], f"one token {w} E={E} k={k} I={I}")
+    r = torch.randn(1, cfg.hidden, dtype=torch.float32, device="cuda")
+    res = c.run(residual=r)
+    assert np.array_equal(res["out"], base["out"] + r.cpu().numpy())
+
+
 # ---- prefill bf16 (grouped MFMA GEMM) ---------------------------------------------------
 
 # T*k above 2048 takes the multi-block counting sort: 1500 x 2 over 4 experts and
