@@ -112,7 +112,8 @@ struct Ptrs {
     uint32_t s;                                   // MX: this thread's scale row within the blob
 };
 
-template <bool MX, int BM, int BNT, int KS, int NTH>
+// BAUX: cache policy of the weight loads (2 = non-temporal, 0 = default).
+template <int BAUX, bool MX, int BM, int BNT, int KS, int NTH>
 __device__ __forceinline__ void gload(Stage<MX, BM, BNT, KS, NTH> &st, const Ptrs<MX, BM, BNT, NTH> &p, rsrc_t ra,
                                       rsrc_t rb, int kt, int tid)
 {
@@ -126,7 +127,7 @@ __device__ __forceinline__ void gload(Stage<MX, BM, BNT, KS, NTH> &st, const Ptr
 #pragma unroll
         for (int q = 0; q < NBL; ++q)
             st.b[sub * NBL + q] = __builtin_bit_cast(
-                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rb, p.b[q], MX ? col / 2 : col * 2, 0));
+                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rb, p.b[q], MX ? col / 2 : col * 2, BAUX));
     }
     // every thread loads (threads past BNT re-read row 0's scales), so the number
     // of loads in flight is the same on every path and the compiler's load
@@ -209,6 +210,11 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_grouped_gemm(
     constexpr int NCB = BNT / (32 * WN);  // 32-column MFMA blocks per wave
     static_assert(NW % WM == 0 && NCB >= (MODE == 1 ? 2 : 1) && NMSMAX >= 1, "wave layout");
     constexpr int BT = MX ? BNT * 2 : BNT * 8;  // 16-B slots of one B sub-tile
+    // bf16 gate/up weights are streamed with non-temporal loads (each k-tile
+    // takes whole 128-B lines of a row; 800 -> 756 us for the 4096-token layer).
+    // MXFP4 k-tiles take 32 B of a line whose rest the next three k-tiles use,
+    // and the bf16 down GEMM got slower with them: default policy there.
+    constexpr int BAUX = (!MX && MODE == 1) ? 2 : 0;
     __shared__ u32x4_t As[2][KS * BM * 8];
     __shared__ u32x4_t Bs[2][KS * BT];
     __shared__ float Scf[2][MX ? 2 * KS * (BNT + 32) : 4];
@@ -295,8 +301,8 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_grouped_gemm(
                 for (int j = 0; j < 16; ++j)
                     acc[a][b][j] = 0.f;
         Stage<MX, BM, BNT, KS, NTH> s0, s1;
-        gload(s0, p, ra, rbs, 0, tid);
-        gload(s1, p, ra, rbs, 1, tid);
+        gload<BAUX>(s0, p, ra, rbs, 0, tid);
+        gload<BAUX>(s1, p, ra, rbs, 1, tid);
         sstore(s0, As[0], Bs[0], Scf[0], tid);
         __syncthreads();
         // NXT holds k-tile kt+1 (loaded one iteration ago); FRE is free and
@@ -309,7 +315,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_grouped_gemm(
 #define ECF_GEMM_BODY(KT, NXT, FRE)                                                                  \
     {                                                                                               \
         const int cur = (KT) & 1;                                                                   \
-        gload(FRE, p, ra, rbs, min((KT) + 2, nk - 1), tid);                                         \
+        gload<BAUX>(FRE, p, ra, rbs, min((KT) + 2, nk - 1), tid);                                   \
         if (NMS > 0) {                                                                              \
             _Pragma("unroll") for (int sub = 0; sub < KS; ++sub)                                    \
             {                                                                                       \
@@ -357,10 +363,12 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_grouped_gemm(
                     for (int cb = 0; cb < NCB / 2; ++cb)
                         H[cb * 32] = f_to_bf(silu_mul(acc[ms][cb][j], acc[ms][cb + NCB / 2][j]));
                 } else {
+                    // Y is read once, by the combine: non-temporal stores (bf16
+                    // down GEMM 491 -> 445 us; MXFP4 unchanged)
                     float *Y = (float *)out + (size_t)(rb + m) * N + n0 + wn * (BNT / WN) + (l & 31);
 #pragma unroll
                     for (int cb = 0; cb < NCB; ++cb)
-                        Y[cb * 32] = acc[ms][cb][j];
+                        __builtin_nontemporal_store(acc[ms][cb][j], Y + cb * 32);
                 }
             }
         }
