@@ -54,9 +54,10 @@ def src_hash(*names):
 # ---- achievable HBM bandwidth on this GPU (context for the roofline's 8 TB/s peak) ----------
 
 def bench_hbm(torch, ecf, reps=10):
-    """A plain streaming read of 4 GiB (libecf's ecf_stream_read: 16 B per lane,
-    eight loads in flight) and a 2 GiB device copy (torch), timed with HIP
-    events: what simple kernels reach on this GPU."""
+    """A plain streaming read of 4 GiB (libecf's ecf_stream_read: one contiguous
+    chunk per block, two blocks per CU, 16 B per lane, eight loads in flight)
+    and a 2 GiB device copy (torch), timed with HIP events: what simple kernels
+    reach on this GPU."""
     n = 1 << 30
     a = torch.empty(n, dtype=torch.float32, device="cuda")  # contents do not matter for timing
     b = torch.empty(n // 2, dtype=torch.float32, device="cuda")

@@ -293,7 +293,8 @@ int ecf_profile_reset(void);
 
 /*
  * One plain streaming read of bytes (a multiple of 16) at d_buf (16-byte
- * aligned), 16 bytes per lane and load, as a yardstick for the HBM bandwidth the
+ * aligned): two blocks per CU, each reading one contiguous chunk front to back,
+ * 16 bytes per lane and load, as a yardstick for the HBM bandwidth the
  * layer's kernels reach; *d_sink ^= the XOR of every 32-bit word read (the
  * caller zeroes it first if it wants the value).  Asynchronous on stream (NULL =
  * null stream); the caller times it.  ECF_EINVAL for bad pointers or sizes.
