@@ -304,3 +304,14 @@ def test_stream_read_argument_checks():
         with pytest.raises(ecf.EcfError) as ei:
             ecf.ecf_stream_read(buf, n, sink)
         assert ei.value.code == ecf.ECF_EINVAL
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 exits with status 2 and says so,
+    before anything touches a GPU."""
+    import subprocess
+    import sys
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert p.returncode == 2
+    assert "one GPU" in p.stdout
