@@ -8,7 +8,7 @@ from .ref import (  # noqa: F401
     ORC_F32, ORC_BF16, ORC_MXFP4,
     lib,
     e2m1, e8m0,
-    logits, route, permute, moe_tokens, moe_layer, expert_ffn,
+    logits, route, permute, moe_tokens, moe_layer, expert_ffn, mxfp4_as_bf16,
     qstar, qstar_closed_form,
     LRURef,
 )

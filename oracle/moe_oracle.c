@@ -76,6 +76,30 @@ double orc_weight(int dtype, const void *w, const uint8_t *scales, long r, long 
     return orc_e2m1(nib) * orc_e8m0(scales[r * (cols / 32) + c / 32]);
 }
 
+/* The same MXFP4 matrix [rows][cols] written as bf16 bit patterns: element
+ * (r, c) is orc_weight's exact value of it, stored in bf16.  An E2M1 value
+ * (at most two significant bits) times 2^(s - 127) fits bf16 exactly for
+ * every scale byte s up to 252 (bf16 has fp32's exponent range); the return
+ * value counts the elements that do not (they are stored rounded), so a
+ * caller that gets 0 holds the very values the MXFP4 path computes with and
+ * can run the bf16 path in their place, fp64 for fp64, at bf16 decoding cost. */
+long orc_mxfp4_to_bf16(const uint8_t *w, const uint8_t *scales, long rows, long cols, uint16_t *out)
+{
+    long bad = 0;
+#pragma omp parallel for schedule(static) reduction(+ : bad)
+    for (long r = 0; r < rows; ++r)
+        for (long c = 0; c < cols; ++c) {
+            double v = orc_weight(ORC_MXFP4, w, scales, r, c, cols);
+            float f = (float)v;
+            uint32_t u;
+            memcpy(&u, &f, sizeof u);
+            if (!isnan(v) && ((double)f != v || (u & 0xffffu) != 0))
+                ++bad;
+            out[r * cols + c] = (uint16_t)(u >> 16);
+        }
+    return bad;
+}
+
 static double act(int a_dtype, const void *x, long r, long c, long cols)
 {
     if (a_dtype == ORC_F32)

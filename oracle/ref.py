@@ -55,6 +55,8 @@ def lib():
         L.orc_permute.argtypes = [P, I32, I32, I32, P, P, P, P]
         L.orc_expert_ffn.argtypes = [I32, P, P, P, P, P, P, I32, I32, P, P]
         L.orc_moe_tokens.argtypes = [I32, I32, P, I32, I32, I32, P, P, P, P, P, P, P, P, P, I32, P]
+        L.orc_mxfp4_to_bf16.argtypes = [P, P, ctypes.c_long, ctypes.c_long, P]
+        L.orc_mxfp4_to_bf16.restype = ctypes.c_long
         for f in ("orc_logits", "orc_route", "orc_permute", "orc_expert_ffn", "orc_moe_tokens"):
             getattr(L, f).restype = None
         _ = F
@@ -182,6 +184,25 @@ def moe_tokens(x, experts, idx, gates, tokens=None, w_dtype: str = "bf16"):
     lib().orc_moe_tokens(_DT[w_dtype], _adt(x), _ptr(x), d, I, k, tab.get("w_gate"), tab.get("w_up"),
                          tab.get("w_down"), sg, tab.get("s_up"), tab.get("s_down"), _ptr(idx),
                          _ptr(gates), _ptr(tokens), len(tokens), _ptr(out))
+    return out
+
+
+def mxfp4_as_bf16(ex) -> dict:
+    """One MXFP4 expert (nibbles + E8M0 scales) as bf16 bit patterns (uint16
+    arrays w_gate [I,d], w_up [I,d], w_down [d,I]) holding exactly the values
+    the oracle's MXFP4 decoding gives, so moe_tokens(..., "bf16") on them
+    computes the MXFP4 layer fp64 for fp64 without decoding every element per
+    token.  Raises if a value does not fit bf16 exactly (scale byte above 252)."""
+    out = {}
+    for nm, sn in (("w_gate", "s_gate"), ("w_up", "s_up"), ("w_down", "s_down")):
+        w, sc = _np(ex[nm]), _np(ex[sn])
+        rows, cols = w.shape[0], w.shape[1] * 2
+        assert sc.shape == (rows, cols // 32)
+        o = np.empty((rows, cols), np.uint16)
+        bad = lib().orc_mxfp4_to_bf16(_ptr(w), _ptr(sc), rows, cols, _ptr(o))
+        if bad:
+            raise ValueError(f"{nm}: {bad} MXFP4 values do not fit bf16 exactly")
+        out[nm] = o
     return out
 
 

@@ -77,6 +77,42 @@ def test_mxfp4_generator_roundtrip_bound():
     assert np.all(amax_code >= 4.0)
 
 
+def test_mxfp4_as_bf16_by_hand_and_exact():
+    # the hand row of test_mxfp4_weight_decode_by_hand, re-encoded: bf16 bits of
+    # 3, -0.25, 0.75, -3, 0 and 24, -16, 4 (exact binary fractions)
+    nib = np.zeros(64, np.uint8)
+    nib[0], nib[1], nib[2], nib[31] = 0x7, 0x9, 0x3, 0xF
+    nib[32], nib[33], nib[63] = 0x5, 0xC, 0x1
+    packed = (nib[0::2] | (nib[1::2] << 4)).astype(np.uint8)[None, :]
+    sc = np.array([[126, 130]], np.uint8)
+    ex = {n: torch.from_numpy(packed.copy()) for n in ("w_gate", "w_up", "w_down")}
+    ex.update({n: torch.from_numpy(sc.copy()) for n in ("s_gate", "s_up", "s_down")})
+    bits = oracle.mxfp4_as_bf16(ex)["w_gate"][0]
+    as_f = lambda b: float(torch.tensor([int(b)], dtype=torch.int32).to(torch.int16).view(torch.bfloat16).float())
+    assert [as_f(bits[c]) for c in (0, 1, 2, 31, 5, 32, 33, 63)] == [3.0, -0.25, 0.75, -3.0, 0.0, 24.0, -16.0, 4.0]
+    # a scale of 2^126 with element 6 (1.5 * 2^128) does not fit bf16: refused
+    big = dict(ex, s_up=torch.full((1, 2), 253, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        oracle.mxfp4_as_bf16(big)
+
+
+def test_mxfp4_layer_equals_its_bf16_reencoding():
+    # the layer on MXFP4 experts and on their exact bf16 re-encoding: the same
+    # fp64 values in the same order, so the outputs are identical bit for bit
+    cfg = syn.gen.Config(93, "t", (9,), 256, 4, 128, 2, "mxfp4", "bf16", "normal_t", temperature=0.5)
+    experts = [syn.expert_weights(cfg, 0, e) for e in range(4)]
+    re = [oracle.mxfp4_as_bf16(ex) for ex in experts]
+    x = syn.activations(cfg, 9)
+    lg = syn.router_logits(cfg, 9)
+    a = oracle.moe_layer(x, experts, 2, lg=lg, w_dtype="mxfp4")
+    b = oracle.moe_layer(x, re, 2, lg=lg, w_dtype="bf16")
+    assert np.array_equal(a["out"], b["out"])
+    for nm in ("w_gate", "w_down"):
+        dense = _mx_dense(experts[1][nm], experts[1]["s" + nm[1:]]).numpy()
+        got = torch.from_numpy(re[1][nm].view(np.int16)).view(torch.bfloat16).double().numpy()
+        assert np.array_equal(got, dense)
+
+
 # ---- router ---------------------------------------------------------------------
 
 def test_logits_bf16_against_fp64_matmul():
