@@ -150,30 +150,93 @@ def test_cache_state_invariance_and_resize():
         cs.close()
 
 
-def test_cached_decode_full_shape_two_layers():
-    """d 4096, 256 experts, I 1024, top-6, T 16, slots = 37% of the (2-layer)
-    pool, Zipf(1.1) routing, q* at B_P/B_H = 0.4; host blobs aliased 32 ways."""
+def _layer_experts(cs, cfg, l):
+    """CPU tensors of layer l's experts as the cache's host pool holds them (aliased blobs)."""
+    E = cfg.experts
+    memo = cs.__dict__.setdefault("_cpu_blobs", {})
+    out = []
+    for e in range(E):
+        b = cs.blob_of(l, e)
+        if b not in memo:
+            memo[b] = {k: v.cpu() for k, v in syn.expert_weights(cfg, b // E, b % E, device="cuda").items()}
+        out.append(memo[b])
+    return out
+
+
+@pytest.mark.parametrize("T", [1, 4, 16])
+def test_cached_decode_full_shape_two_layers(T):
+    """d 4096, 256 experts, I 1024, top-6, slots = 37% of the (2-layer) pool,
+    Zipf(1.1) routing, q* at B_P/B_H = 0.4, host blobs aliased 32 ways: every
+    step's cache-mode output (GPU experts + host experts + host partial) against
+    the oracle within the bf16 bar, routing and counts exact, and against the
+    all-resident layer within 1e-5."""
     base = syn.CONFIGS["cached"]
-    L, T, d = 2, 16, base.hidden
+    L, d, k, E = 2, base.hidden, base.top_k, base.experts
     n_slots = int(0.37 * L * base.experts)
-    say(f"case: cached decode full shape, {n_slots} slots")
+    say(f"case: cached decode full shape T={T}, {n_slots} slots")
     cs = CachedSetup(base, L, n_slots=n_slots, n_blobs=32, gen_device="cuda")
     lay = Layer(cs.shape, T)
     cstream = torch.cuda.Stream()
     try:
+        host_total = 0
         for step in range(6):
             l = step % L
             x = syn.activations(base, T, layer=l, batch=step, device="cuda")
             lg = syn.router_logits(base, T, layer=l, step=step, device="cuda")
             ref, _ = _run(lay, lay.args(layer=l, router_logits=lg, expert_ptrs=cs.resident_ptrs[l]), x, T, d)
+            idx = torch.full((T * k,), -1, dtype=torch.int32, device="cuda")
+            counts = torch.full((E,), -1, dtype=torch.int32, device="cuda")
             got, st = _run(lay, lay.args(layer=l, router_logits=lg, cache=cs.cache, b_p=0.4, b_h=1.0,
-                                         copy_stream=cstream), x, T, d)
+                                         copy_stream=cstream, topk_idx=idx, counts=counts), x, T, d)
+            host_total += st["host"]
+            orc = oracle.moe_layer(x.cpu(), _layer_experts(cs, base, l), k, lg=lg.cpu())
+            assert np.array_equal(idx.cpu().numpy().reshape(T, k), orc["idx"])
+            assert np.array_equal(counts.cpu().numpy(), orc["counts"])
+            rms = np.sqrt(np.mean(orc["out"] ** 2))
+            e_orc = np.max(np.abs(got - orc["out"])) / rms
             err = np.max(np.abs(got - ref)) / np.sqrt(np.mean(ref ** 2))
             say(f"step {step}: unique={st['n_unique']} hits={st['hits']} m={st['misses']} q={st['q']} "
                 f"host={st['host']} wait={st['ms_wait_route']:.2f}ms host_ffn={st['ms_host_ffn']:.2f}ms "
-                f"err/RMS={err:.2e}")
+                f"err/RMS vs resident {err:.2e}, vs oracle {e_orc:.2e}")
             assert st["q"] == ecf.qstar_split(st["misses"], 0.4, 1.0)
             assert err <= SPLIT_TOL
+            assert e_orc <= 2e-2
+        assert host_total > 0  # the host half of the split ran
+    finally:
+        cs.close()
+
+
+def test_stack_three_layers_against_oracle():
+    """Three stacked layers in cache mode (q* at 0.4, host experts on): the residual
+    stream stays fp32 (out = residual + MoE(x)) and each layer's input is the
+    previous output rounded to bf16 (d_out_act).  Layer by layer, the GPU output
+    equals the GPU's residual input plus the oracle's layer on the GPU's own bf16
+    input, within 2e-2 of that layer's RMS, and the bf16 copy is the output
+    rounded to nearest even."""
+    cfg = syn.gen.Config(103, "stack", (6,), 512, 16, 256, 4, "bf16", "bf16", "zipf", layers=3)
+    L, T, d, k = 3, 6, cfg.hidden, cfg.top_k
+    cs = CachedSetup(cfg, L, n_slots=12)
+    lay = Layer(cs.shape, T)
+    cstream = torch.cuda.Stream()
+    try:
+        x = syn.activations(cfg, T, device="cuda")
+        res_f = x.float().clone()
+        act = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
+        for l in range(L):
+            lg = syn.router_logits(cfg, T, layer=l, device="cuda")
+            x_in, r_in = x.cpu().clone(), res_f.cpu().numpy().copy()
+            a = lay.args(layer=l, router_logits=lg, cache=cs.cache, b_p=0.4, b_h=1.0, copy_stream=cstream,
+                         residual=res_f, out_act=act)
+            st = lay.forward(a, x, res_f)
+            torch.cuda.synchronize()
+            out = res_f.cpu().numpy()
+            moe = oracle.moe_layer(x_in, _layer_experts(cs, cfg, l), k, lg=lg.cpu())["out"]
+            rms = np.sqrt(np.mean(moe ** 2))
+            err = np.max(np.abs(out - (r_in + moe))) / rms
+            say(f"stack layer {l}: m={st['misses']} q={st['q']} host={st['host']} err/RMS {err:.2e}")
+            assert err <= 2e-2
+            assert torch.equal(act.cpu(), res_f.cpu().to(torch.bfloat16))
+            x = act.clone()
     finally:
         cs.close()
 
