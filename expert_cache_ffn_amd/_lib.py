@@ -24,7 +24,8 @@ EXPORTS = [
     "ecf_last_error", "ecf_expert_bytes", "ecf_expert_layout", "ecf_workspace_bytes", "qstar_split",
     "ecf_cache_create", "ecf_cache_destroy", "expert_cache_lookup", "expert_cache_evict",
     "ecf_cache_available", "ecf_cache_slot_of", "ecf_cache_get_stats", "ecf_cache_resize",
-    "prefetch_layer", "moe_layer_forward", "ecf_host_experts", "ecf_bandwidth_profile", "ecf_profile_enable",
+    "prefetch_layer", "moe_layer_forward", "moe_layer_forward_noalloc", "ecf_noalloc_scratch_bytes",
+    "ecf_host_experts", "ecf_bandwidth_profile", "ecf_profile_enable",
     "ecf_profile_get", "ecf_profile_reset", "ecf_stream_read",
 ]
 
@@ -110,6 +111,10 @@ def lib():
         L.prefetch_layer.restype = c_int32
         L.moe_layer_forward.argtypes = [POINTER(LayerArgs), c_void_p, c_int32, c_void_p, POINTER(StepStats)]
         L.moe_layer_forward.restype = c_int32
+        L.moe_layer_forward_noalloc.argtypes = [POINTER(LayerArgs), c_void_p, c_int32, c_void_p,
+                                                POINTER(StepStats)]
+        L.moe_layer_forward_noalloc.restype = c_int32
+        L.ecf_noalloc_scratch_bytes.argtypes, L.ecf_noalloc_scratch_bytes.restype = [], c_size_t
         L.ecf_host_experts.argtypes = [POINTER(Shape), c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                                        c_void_p, c_int32]
         L.ecf_host_experts.restype = c_int32
@@ -230,6 +235,18 @@ def moe_layer_forward(args: LayerArgs, d_x, n_tokens, d_out, want_stats=True):
                                    c_void_p(int(d_out)) if d_out else None,
                                    ctypes.byref(st) if want_stats else None))
     return st.as_dict() if want_stats else None
+
+
+def moe_layer_forward_noalloc(args: LayerArgs, d_x, n_tokens, d_out, want_stats=True):
+    st = StepStats()
+    _check(lib().moe_layer_forward_noalloc(ctypes.byref(args), c_void_p(int(d_x)) if d_x else None,
+                                           int(n_tokens), c_void_p(int(d_out)) if d_out else None,
+                                           ctypes.byref(st) if want_stats else None))
+    return st.as_dict() if want_stats else None
+
+
+def ecf_noalloc_scratch_bytes() -> int:
+    return int(lib().ecf_noalloc_scratch_bytes())
 
 
 def ecf_host_experts(shape: Shape, blob_ptrs, rows_per_job, x_ptr, n_tokens, y_ptr, n_threads=0):

@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libecf.so")
 BUILD = os.path.join(os.path.dirname(HERE), "_build")
 
-HIP_SRCS = ["k_route.hip", "k_decode.hip", "k_prefill.hip", "k_util.hip"]
+HIP_SRCS = ["k_route.hip", "k_decode.hip", "k_prefill.hip", "k_util.hip", "noalloc.hip"]
 CPP_SRCS = ["api.cpp", "cache.cpp", "qstar.cpp", "host_ffn.cpp", "bwprof.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -78,9 +78,11 @@ int prof_resolve()
 }
 }  // namespace
 
+thread_local bool t_prof_quiet = false;
+
 ProfScope::ProfScope(const char *name, hipStream_t s) : name_(name), s_(s)
 {
-    if (!g_prof_on)
+    if (!g_prof_on || t_prof_quiet)
         return;
     if (hipEventCreate(&a_) != hipSuccess) {
         a_ = nullptr;
@@ -527,8 +529,15 @@ static int cache_step(const ecf_layer_args *a, const void *d_x, int32_t T, const
     return ECF_OK;
 }
 
-int moe_layer_forward(const ecf_layer_args *a, const void *d_x, int32_t T, float *d_out,
-                      ecf_step_stats *stats)
+}  // extern "C"
+
+namespace ecf {
+
+// The forward call with its workspace given explicitly (ws, ws_bytes): the
+// caller's buffer for moe_layer_forward, the library's own device array for
+// moe_layer_forward_noalloc.
+int forward_impl(const ecf_layer_args *a, const void *d_x, int32_t T, float *d_out, ecf_step_stats *stats,
+                 void *d_ws, size_t ws_bytes)
 {
     try {
         if (!a)
@@ -543,19 +552,19 @@ int moe_layer_forward(const ecf_layer_args *a, const void *d_x, int32_t T, float
             std::memset(stats, 0, sizeof *stats);
         if (T == 0)
             return ECF_OK;
-        if (!d_x || !d_out || !a->d_ws)
+        if (!d_x || !d_out || !d_ws)
             return set_error(ECF_EINVAL, "x, out and workspace must be given");
         if ((a->d_router_w == nullptr) == (a->d_router_logits == nullptr))
             return set_error(ECF_EINVAL, "give exactly one of d_router_w and d_router_logits");
         if ((a->d_expert_ptrs == nullptr) == (a->cache == nullptr))
             return set_error(ECF_EINVAL, "give exactly one of d_expert_ptrs and cache");
-        if ((uintptr_t)a->d_ws % 256)
+        if ((uintptr_t)d_ws % 256)
             return set_error(ECF_EINVAL, "workspace must be 256-byte aligned");
         if ((uintptr_t)d_x % 16)
             return set_error(ECF_EINVAL, "x must be 16-byte aligned");
         const WsLayout wl = ws_layout(s, T);
-        if (a->ws_bytes < wl.total)
-            return set_error(ECF_ENOSPC, "workspace too small: %zu < %zu bytes for %d tokens", a->ws_bytes,
+        if (ws_bytes < wl.total)
+            return set_error(ECF_ENOSPC, "workspace too small: %zu < %zu bytes for %d tokens", ws_bytes,
                              wl.total, T);
         const int path = pick_path(a, T);
         if (path == ECF_PATH_PREFILL && (s.w_dtype == ECF_F32 || s.inter % 128))
@@ -565,7 +574,7 @@ int moe_layer_forward(const ecf_layer_args *a, const void *d_x, int32_t T, float
                              "cache mode runs the decode GEMVs (the prefill GEMM's bf16 h would make the "
                              "output depend on the split)");
         hipStream_t stream = (hipStream_t)a->stream;
-        char *ws = (char *)a->d_ws;
+        char *ws = (char *)d_ws;
         BlobLayout lay;
         blob_layout(s, &lay);
 
@@ -633,4 +642,10 @@ int moe_layer_forward(const ecf_layer_args *a, const void *d_x, int32_t T, float
     }
 }
 
-}  // extern "C"
+}  // namespace ecf
+
+extern "C" int moe_layer_forward(const ecf_layer_args *a, const void *d_x, int32_t T, float *d_out,
+                                 ecf_step_stats *stats)
+{
+    return forward_impl(a, d_x, T, d_out, stats, a ? a->d_ws : nullptr, a ? a->ws_bytes : 0);
+}

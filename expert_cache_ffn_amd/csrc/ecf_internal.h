@@ -46,6 +46,15 @@ struct ProfScope {
     hipEvent_t a_ = nullptr, b_ = nullptr;
 };
 
+// While set on a thread, ProfScope records nothing there (no events created):
+// the allocation-free forward call sets it for its duration.
+extern thread_local bool t_prof_quiet;
+
+// The layer forward on an explicit workspace (moe_layer_forward passes the
+// caller's, moe_layer_forward_noalloc the library's own device array).
+int forward_impl(const ecf_layer_args *a, const void *d_x, int32_t T, float *d_out, ecf_step_stats *stats,
+                 void *d_ws, size_t ws_bytes);
+
 // ---- geometry ------------------------------------------------------------------
 constexpr int64_t kMaxRows = (int64_t)1 << 26;  // n_tokens * top_k per call (row indices are 32-bit)
 constexpr int kSortSeg = 1024;      // rows per segment of the multi-block counting sort

@@ -240,6 +240,26 @@ int moe_layer_forward(const ecf_layer_args *args, const void *d_x, int32_t n_tok
                       ecf_step_stats *stats);
 
 /*
+ * Allocation-free variant of moe_layer_forward, for callers that cannot
+ * allocate device memory or call anything that does: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments and results as moe_layer_forward in all-resident mode, except
+ * that args->d_ws and args->ws_bytes are ignored: the workspace is a device
+ * array inside the library, ecf_noalloc_scratch_bytes() bytes (32 MiB) per GPU,
+ * held until the process ends.  The call allocates nothing and records no
+ * profiling events.  ECF_ENOSPC if ecf_workspace_bytes(shape, n_tokens)
+ * exceeds that size (about 230 tokens of a d 4096 / E 256 / I 1024 / top-6
+ * layer); ECF_EUNSUPPORTED in cache mode (args->cache non-NULL).  Every call on
+ * one GPU shares that GPU's array (the current device's at the call), and the
+ * array keeps the last call's contents: calls that overlap on one GPU (other
+ * streams or threads) race and must be serialised by the caller.
+ */
+int moe_layer_forward_noalloc(const ecf_layer_args *args, const void *d_x, int32_t n_tokens,
+                              float *d_out, ecf_step_stats *stats);
+/* Bytes of the per-GPU array moe_layer_forward_noalloc uses as its workspace. */
+size_t ecf_noalloc_scratch_bytes(void);
+
+/*
  * The host half of the split on its own: y[f][:] = FFN_e(x[f / k]) for the rows
  * f listed per expert, evaluated by n_threads host threads (0 = default) the
  * same way a forward call evaluates host-assigned experts [TF "Bandwidth-
