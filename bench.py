@@ -374,21 +374,38 @@ def cpu_oracle_prefill(torch, syn, cfg, x, lg, counts_gpu, out_gpu, sample=128):
     return r
 
 
-def bench_prefill(torch, ecf, syn, name, steps, warmup, cpu=False):
-    from expert_cache_ffn_amd.layer import ExpertPool, Layer
+def bench_prefill(torch, ecf, syn, name, steps, warmup, cpu=False, host_inputs=False):
+    from expert_cache_ffn_amd.layer import ExpertPool, Layer, pack_expert
     cfg = syn.CONFIGS[name]
     T, d, E, I, k = cfg.tokens[0], cfg.hidden, cfg.experts, cfg.inter, cfg.top_k
     shape = ecf.make_shape(d, I, E, k, cfg.w_dtype, "bf16")
     S = ecf.ecf_expert_bytes(shape)
-    log(f"{name}: generating {E} experts ({E * S / 1e9:.2f} GB, {cfg.w_dtype}) on the GPU")
     pool = ExpertPool(shape, "cuda")
-    for e in range(E):
-        pool.load(e, syn.expert_weights(cfg, 0, e, device="cuda"))
+    # host_inputs: every input is generated on the host and copied in, so the only
+    # GPU kernels of the run are libecf's (a hardware counter pass then sees
+    # nothing else); the expert blobs repeat HOST_EXPERTS host-generated experts,
+    # routing inputs are the full recipe's (timing and traffic do not depend on
+    # weight values)
+    gen_dev = "cpu" if host_inputs else "cuda"
+    if host_inputs:
+        log(f"{name}: {E} expert blobs ({E * S / 1e9:.2f} GB, {cfg.w_dtype}) from {HOST_EXPERTS} host-generated experts")
+        blobs = []
+        for h in range(HOST_EXPERTS):
+            b = torch.empty(S, dtype=torch.uint8)
+            pack_expert(shape, syn.expert_weights(cfg, 0, h, device="cpu"), b)
+            blobs.append(b)
+        for e in range(E):
+            pool.buf[e].copy_(blobs[e % HOST_EXPERTS])
+        del blobs
+    else:
+        log(f"{name}: generating {E} experts ({E * S / 1e9:.2f} GB, {cfg.w_dtype}) on the GPU")
+        for e in range(E):
+            pool.load(e, syn.expert_weights(cfg, 0, e, device="cuda"))
     lay = Layer(shape, T)
-    xs = [syn.activations(cfg, T, batch=b, device="cuda") for b in range(2)]
-    lgs = [syn.router_logits(cfg, T, step=b, device="cuda") for b in range(2)]
+    xs = [syn.activations(cfg, T, batch=b, device=gen_dev).to("cuda") for b in range(2)]
+    lgs = [syn.router_logits(cfg, T, step=b, device=gen_dev).to("cuda") for b in range(2)]
     out = torch.empty((T, d), dtype=torch.float32, device="cuda")
-    counts = torch.zeros(E, dtype=torch.int32, device="cuda")
+    counts = torch.zeros(E, dtype=torch.int32).to("cuda")
     argsv = [lay.args(router_logits=lgs[b], expert_ptrs=pool.ptrs) for b in range(2)]
     call = lambda i: ecf.lib().moe_layer_forward(argsv[i % 2], xs[i % 2].data_ptr(), T, out.data_ptr(), None)
     lay.forward(lay.args(router_logits=lgs[0], expert_ptrs=pool.ptrs, counts=counts), xs[0], out, False)
@@ -419,7 +436,7 @@ def bench_prefill(torch, ecf, syn, name, steps, warmup, cpu=False):
     kern = {n: {"launches": c, "avg_us": 1e3 * t / max(c, 1)} for n, (c, t) in prof.items()}
     R = T * k
     flops = 2.0 * R * d * 3 * I
-    n_active = int((counts > 0).sum())
+    n_active = int((counts.cpu() > 0).sum())
     wbytes = n_active * S
     res = dict(tokens=T, ms_per_layer=ms, tokens_per_s=T / (ms * 1e-3), active_experts=n_active,
                ms_median=per_step[steps // 2], ms_p10=per_step[steps // 10],
@@ -432,7 +449,7 @@ def bench_prefill(torch, ecf, syn, name, steps, warmup, cpu=False):
     if g1 and g2:
         res["gemm1_tflops"] = 2.0 * R * d * 2 * I / (g1 * 1e-6) / 1e12
         res["gemm2_tflops"] = 2.0 * R * I * d / (g2 * 1e-6) / 1e12
-    if cpu:  # the oracle beside it, on batch 0 (what `counts` holds)
+    if cpu and not host_inputs:  # the oracle beside it, on batch 0 (what `counts` holds)
         lay.forward(lay.args(router_logits=lgs[0], expert_ptrs=pool.ptrs), xs[0], out, False)
         torch.cuda.synchronize()
         # MXFP4 expert FFNs take the oracle ~0.15 s per token: a smaller sample
@@ -446,71 +463,118 @@ def bench_prefill(torch, ecf, syn, name, steps, warmup, cpu=False):
     return res
 
 
-def bench_prefetch(torch, ecf, syn, layers=4):
-    """Prefill stack: layer l computes from one half of a 2-layer buffer while
-    layer l+1's whole expert blob streams from pinned host into the other."""
+def bench_prefetch(torch, ecf, syn, name="prefill", layers=8, reps=3):
+    """Prefill stack through the shared slot pool: before layer l's forward call,
+    prefetch_layer queues layer l+1's whole expert set (one contiguous host layer
+    blob) into the cache's slots on a copy stream; the forward call of l+1 waits
+    on device for it.  Slots: two layers.  Host pool: two distinct pinned layer
+    blobs, aliased over the stack.  Timed with HIP events: the copy of a layer
+    alone (median of `reps` warm copies), the layer's forward alone on resident
+    slots (median of `reps`), and the stack.  From the start of layer 1's copy
+    to the end of the last layer's copy the copy stream moves L-1 layers
+    (t_copy per layer); from the same start to the end of the last layer's
+    kernels the stack finishes L-1 layers (t_layer per layer); the last layer
+    waits for its copy, so t_copy <= t_layer by construction.  overlap =
+    max(t_copy, compute alone) / t_layer (1 = the shorter of the two is wholly
+    hidden)."""
     from expert_cache_ffn_amd.layer import Layer, pack_expert
-    cfg = syn.CONFIGS["prefill"]
+    cfg = syn.CONFIGS[name]
     T, d, E, I, k = cfg.tokens[0], cfg.hidden, cfg.experts, cfg.inter, cfg.top_k
-    shape = ecf.make_shape(d, I, E, k, "bf16", "bf16")
+    shape = ecf.make_shape(d, I, E, k, cfg.w_dtype, "bf16")
     S = ecf.ecf_expert_bytes(shape)
     LB = E * S
-    log(f"prefetch: pinning 2 host layer blobs ({2 * LB / 1e9:.1f} GB), 2-layer device buffer")
-    host = [torch.empty(LB, dtype=torch.uint8).pin_memory() for _ in range(2)]
-    buf = torch.empty(2 * LB, dtype=torch.uint8, device="cuda")
+    log(f"{name} stream: pinning 2 host layer blobs ({2 * LB / 1e9:.1f} GB), {2 * E} slots ({2 * LB / 1e9:.1f} GB)")
+    host = torch.empty((2, E, S), dtype=torch.uint8).pin_memory()
+    slots = torch.empty((2 * E, S), dtype=torch.uint8, device="cuda")
     for h in range(2):
         for e in range(E):
-            pack_expert(shape, syn.expert_weights(cfg, h, e, device="cuda"), buf[e * S:(e + 1) * S])
-        host[h].copy_(buf[:LB].cpu())
-    ptrs = [torch.tensor([buf.data_ptr() + half * LB + e * S for e in range(E)], dtype=torch.int64, device="cuda")
-            for half in range(2)]
+            pack_expert(shape, syn.expert_weights(cfg, h, e, device="cuda"), slots[e])
+        host[h].copy_(slots[:E].cpu())
+    hb = host.data_ptr()
+    pool = [hb + ((l % 2) * E + e) * S for l in range(layers) for e in range(E)]
+    cache = ecf.ecf_cache_create(layers, E, 2 * E, 2 * E, S, slots.data_ptr(), pool, host_threads=1)
     lay = Layer(shape, T)
-    x = syn.activations(cfg, T, device="cuda")
-    lg = syn.router_logits(cfg, T, device="cuda")
-    out = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    xs = [syn.activations(cfg, T, layer=l % 2, device="cuda") for l in range(2)]
+    lgs = [syn.router_logits(cfg, T, layer=l % 2, device="cuda") for l in range(2)]
+    outs = [torch.empty((T, d), dtype=torch.float32, device="cuda") for _ in range(layers)]
     comp, copy = torch.cuda.current_stream(), torch.cuda.Stream()
-    ready = [torch.cuda.Event() for _ in range(2)]
-    free = [torch.cuda.Event() for _ in range(2)]
-    torch.cuda.synchronize()  # setup queued on the default stream must land before the copy stream writes buf
-    # copy alone
-    t0 = time.perf_counter()
-    ecf.prefetch_layer(host[0].data_ptr(), buf.data_ptr(), LB, LB, copy.cuda_stream, 0)
-    copy.synchronize()
-    t_copy = time.perf_counter() - t0
-    # compute alone
-    a = [lay.args(router_logits=lg, expert_ptrs=ptrs[h]) for h in range(2)]
-    lay.forward(a[0], x, out, False)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    args = lambda l: lay.args(layer=l, router_logits=lgs[l % 2], cache=cache, path=ecf.ECF_PATH_PREFILL,
+                              copy_stream=copy)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(3):
-        lay.forward(a[0], x, out, False)
+    med = lambda v: sorted(v)[len(v) // 2]
+    # copy alone: drop every entry (resize to 0 and back), then one whole layer
+    t_copy_solo = []
+    for _ in range(reps):
+        ecf.ecf_cache_resize(cache, 0)
+        ecf.ecf_cache_resize(cache, 2 * E)
+        a, b = ev(), ev()
+        a.record(copy)
+        ecf.prefetch_layer(cache, 0, S, copy.cuda_stream)
+        b.record(copy)
+        b.synchronize()
+        t_copy_solo.append(a.elapsed_time(b))
+    # compute alone: layer 0 resident in its slots (all hits)
+    lay.forward(args(0), xs[0], outs[0], want_stats=False)
+    t_gemm = []
+    for _ in range(reps):
+        a, b = ev(), ev()
+        a.record(comp)
+        lay.forward(args(0), xs[0], outs[0], want_stats=False)
+        b.record(comp)
+        b.synchronize()
+        t_gemm.append(a.elapsed_time(b))
+    # the stack, from an empty cache
+    ecf.ecf_cache_resize(cache, 0)
+    ecf.ecf_cache_resize(cache, 2 * E)
     torch.cuda.synchronize()
-    t_gemm = (time.perf_counter() - t0) / 3
-    # double-buffered stack
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ecf.prefetch_layer(host[0].data_ptr(), buf.data_ptr(), LB, LB, copy.cuda_stream, 0)
-    ready[0].record(copy)
+    c0 = [ev() for _ in range(layers)]
+    c1 = [ev() for _ in range(layers)]
+    done = [ev() for _ in range(layers)]
+    t0 = ev()
+    t0.record(comp)
+    c0[0].record(copy)
+    ecf.prefetch_layer(cache, 0, S, copy.cuda_stream)
+    c1[0].record(copy)
+    n_missing = 0
     for l in range(layers):
-        h = l % 2
         if l + 1 < layers:
-            nh = (l + 1) % 2
-            if l >= 1:
-                copy.wait_event(free[nh])           # layer l-1 finished reading that half
-            ecf.prefetch_layer(host[nh].data_ptr(), buf.data_ptr() + nh * LB, LB, LB, copy.cuda_stream, 0)
-            ready[nh].record(copy)
-        comp.wait_event(ready[h])
-        lay.forward(a[h], x, out, False)
-        free[h].record(comp)
+            c0[l + 1].record(copy)
+            _, m = ecf.prefetch_layer(cache, l + 1, S, copy.cuda_stream)
+            n_missing += m
+            c1[l + 1].record(copy)
+        lay.forward(args(l), xs[l % 2], outs[l], want_stats=False)
+        done[l].record(comp)
     torch.cuda.synchronize()
-    t_stack = (time.perf_counter() - t0) / layers
-    res = dict(layers=layers, layer_bytes=LB, ms_copy=1e3 * t_copy, h2d_GBps=LB / t_copy / 1e9,
-               ms_compute=1e3 * t_gemm, ms_per_layer_streamed=1e3 * t_stack,
-               overlap_efficiency=max(t_copy, t_gemm) / t_stack,
-               tokens_per_s_streamed=T / t_stack)
-    log(f"prefetch: copy {1e3 * t_copy:.1f} ms ({res['h2d_GBps']:.1f} GB/s), compute {1e3 * t_gemm:.2f} ms, "
-        f"streamed {1e3 * t_stack:.1f} ms/layer, overlap {res['overlap_efficiency']:.3f}")
-    del buf, host
+    copies = [c0[l].elapsed_time(c1[l]) for l in range(1, layers)]
+    gaps = [done[l - 1].elapsed_time(done[l]) for l in range(1, layers)]
+    t_copy = c0[1].elapsed_time(c1[-1]) / (layers - 1)
+    t_layer = c0[1].elapsed_time(done[-1]) / (layers - 1)
+    t_comp = med(t_gemm)
+    total = t0.elapsed_time(done[-1])
+    # the last layer against the all-resident prefill on the same slots
+    ptrs = torch.tensor([slots.data_ptr() + ecf.ecf_cache_slot_of(cache, layers - 1, e) * S for e in range(E)],
+                        dtype=torch.int64, device="cuda")
+    ref = torch.empty_like(outs[-1])
+    lay.forward(lay.args(router_logits=lgs[(layers - 1) % 2], expert_ptrs=ptrs, path=ecf.ECF_PATH_PREFILL),
+                xs[(layers - 1) % 2], ref, want_stats=False)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(ref, outs[-1]))
+    st = ecf.ecf_cache_get_stats(cache)
+    ecf.ecf_cache_destroy(cache)
+    res = dict(config=name, layers=layers, tokens=T, layer_bytes=LB, slots=2 * E,
+               ms_copy_solo_median=med(t_copy_solo), ms_copy_solo_all=t_copy_solo,
+               ms_copy_per_layer=t_copy, h2d_GBps=LB / (t_copy * 1e-3) / 1e9,
+               ms_copy_in_stack_median=med(copies), ms_layer_interval_median=med(gaps),
+               ms_compute_median=t_comp, ms_per_layer_streamed=t_layer, ms_stack_total=total,
+               overlap_efficiency=max(t_copy, t_comp) / t_layer,
+               tokens_per_s_streamed=T / (t_layer * 1e-3), experts_not_prefetched=n_missing,
+               last_layer_equals_resident=same, cache_stats=st)
+    log(f"{name} stream: copy {t_copy:.2f} ms/layer in the stack ({res['h2d_GBps']:.1f} GB/s; alone "
+        f"{res['ms_copy_solo_median']:.1f}), compute alone {t_comp:.2f} ms, {t_layer:.2f} ms/layer streamed, "
+        f"overlap {res['overlap_efficiency']:.4f}, last layer {'equals' if same else 'DIFFERS from'} the "
+        f"resident layer")
+    del slots, host
     torch.cuda.empty_cache()
     return res
 
@@ -691,8 +755,10 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run one plain 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--host-inputs", action="store_true",
-                    help="decode: generate inputs on the host (no GPU kernels but libecf's and copies; "
+                    help="decode and prefill: generate inputs on the host (no GPU kernels but libecf's and copies; "
                          "expert blobs repeat a few distinct experts) - for hardware counter passes")
+    ap.add_argument("--prefill-steps", type=int, default=None,
+                    help="prefill layers per timed loop (default max(20, steps / 10))")
     ap.add_argument("--decode-tokens", default="1,4,16",
                     help="decode batch sizes (the headline is 16; others are reported alongside)")
     args = ap.parse_args()
@@ -729,12 +795,15 @@ def main():
                                host_inputs=args.host_inputs, w_dtype="mxfp4")
         also.update({f"decode_mxfp4_T{T}": dec4[T] for T in dec4})
         torch.cuda.empty_cache()
+    psteps = args.prefill_steps or max(20, args.steps // 10)
     if "prefill" in wl:
-        also["prefill_bf16_T4096"] = bench_prefill(torch, ecf, syn, "prefill", max(20, args.steps // 10),
-                                                   max(2, args.warmup // 5), cpu=not args.no_cpu_baseline)
+        also["prefill_bf16_T4096"] = bench_prefill(torch, ecf, syn, "prefill", psteps,
+                                                   max(2, args.warmup // 5), cpu=not args.no_cpu_baseline,
+                                                   host_inputs=args.host_inputs)
     if "prefill_fp4" in wl:
-        also["prefill_mxfp4_T8192"] = bench_prefill(torch, ecf, syn, "prefill_fp4", max(20, args.steps // 10),
-                                                    max(2, args.warmup // 5), cpu=not args.no_cpu_baseline)
+        also["prefill_mxfp4_T8192"] = bench_prefill(torch, ecf, syn, "prefill_fp4", psteps,
+                                                    max(2, args.warmup // 5), cpu=not args.no_cpu_baseline,
+                                                    host_inputs=args.host_inputs)
     if "vendor" in wl:
         also["vendor_bmm_calibration"] = bench_vendor_gemm(torch)
     if sample is not None and not args.no_cpu_baseline:
@@ -744,7 +813,8 @@ def main():
     del sample
     torch.cuda.empty_cache()
     if "prefetch" in wl:
-        also["prefill_prefetch_stack"] = bench_prefetch(torch, ecf, syn)
+        also["prefill_bf16_streamed_stack"] = bench_prefetch(torch, ecf, syn, "prefill")
+        also["prefill_mxfp4_streamed_stack"] = bench_prefetch(torch, ecf, syn, "prefill_fp4")
     if wl & {"cached", "bandwidth", "policies"}:
         cw = args.cached_steps if args.cached_warmup is None else args.cached_warmup
         ctx = cached_setup(torch, ecf, syn, steps=args.cached_steps, warmup=cw)

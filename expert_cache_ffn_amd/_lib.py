@@ -107,7 +107,8 @@ def lib():
         L.ecf_cache_get_stats.argtypes = [c_void_p, POINTER(CacheStats)]
         L.ecf_cache_get_stats.restype = c_int32
         L.ecf_cache_resize.argtypes, L.ecf_cache_resize.restype = [c_void_p, c_int32], c_int32
-        L.prefetch_layer.argtypes = [c_void_p, c_void_p, c_size_t, c_size_t, c_void_p, c_void_p]
+        L.prefetch_layer.argtypes = [c_void_p, c_int32, c_size_t, c_void_p, c_void_p, POINTER(c_int32),
+                                     POINTER(c_int32)]
         L.prefetch_layer.restype = c_int32
         L.moe_layer_forward.argtypes = [POINTER(LayerArgs), c_void_p, c_int32, c_void_p, POINTER(StepStats)]
         L.moe_layer_forward.restype = c_int32
@@ -223,10 +224,14 @@ def ecf_cache_resize(cache, n_slots):
     _check(lib().ecf_cache_resize(c_void_p(cache), int(n_slots)))
 
 
-def prefetch_layer(h_layer_blob, d_buf, nbytes, buf_capacity, copy_stream=0, done_event=0):
-    _check(lib().prefetch_layer(c_void_p(int(h_layer_blob)), c_void_p(int(d_buf)), int(nbytes),
-                                int(buf_capacity), c_void_p(int(copy_stream)) if copy_stream else None,
-                                c_void_p(int(done_event)) if done_event else None))
+def prefetch_layer(cache, layer, blob_bytes, copy_stream=0, done_event=0):
+    """Returns (experts copied, experts that did not fit)."""
+    nc, nm = c_int32(), c_int32()
+    _check(lib().prefetch_layer(c_void_p(cache), int(layer), int(blob_bytes),
+                                c_void_p(int(copy_stream)) if copy_stream else None,
+                                c_void_p(int(done_event)) if done_event else None, ctypes.byref(nc),
+                                ctypes.byref(nm)))
+    return nc.value, nm.value
 
 
 def moe_layer_forward(args: LayerArgs, d_x, n_tokens, d_out, want_stats=True):

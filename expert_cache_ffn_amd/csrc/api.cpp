@@ -185,7 +185,7 @@ WsLayout ws_layout(const ecf_shape &s, int32_t T)
     w.n_tiles = take(4);
     w.seg_counts = take(4 * S * E);
     w.seg_base = take(4 * S * E);
-    w.ptrs = take(8 * E);
+    w.ptrs = take(3 * 8 * E);  // cache mode: hits, copied misses, both
     w.hbuf = take(4 * R * I);
     w.ybuf = take(4 * R * d);
     w.host_out = take(4 * (size_t)T * d);
@@ -210,6 +210,19 @@ int staging(ecf_cache::Staging &s, size_t bytes)
 
 void cache_release_host(ecf_cache *c)
 {
+    // pending prefetch copies still write into the caller's slot memory
+    while (!c->prefetched.empty()) {
+        hipEvent_t ev = cache_take_prefetch(c, c->prefetched.front().layer);
+        if (ev) {
+            (void)hipEventSynchronize(ev);
+            (void)hipEventDestroy(ev);
+        }
+    }
+    for (hipEvent_t ev : c->spare_events)
+        (void)hipEventDestroy(ev);
+    c->spare_events.clear();
+    if (c->last_compute)
+        (void)hipEventDestroy(c->last_compute);
     for (auto *s : {&c->st_counts, &c->st_idx, &c->st_gate, &c->st_x, &c->st_out, &c->st_ptrs, &c->st_y})
         if (s->p)
             (void)hipHostFree(s->p);
@@ -257,22 +270,107 @@ size_t ecf_workspace_bytes(const ecf_shape *shape, int32_t max_tokens)
     return ws_layout(*shape, max_tokens).total;
 }
 
-int prefetch_layer(const void *h_layer_blob, void *d_buf, size_t bytes, size_t buf_capacity,
-                   void *copy_stream, void *done_event)
+int prefetch_layer(ecf_cache *c, int32_t layer, size_t blob_bytes, void *copy_stream, void *done_event,
+                   int32_t *n_copied, int32_t *n_missing)
 {
     return ::ecf::guarded("prefetch_layer", [&]() -> int {
-        if (!h_layer_blob || !d_buf)
-            return set_error(ECF_EINVAL, "prefetch_layer: NULL buffer");
-        if (bytes > buf_capacity)
-            return set_error(ECF_ENOSPC, "prefetch_layer: %zu bytes do not fit a %zu-byte buffer", bytes,
-                             buf_capacity);
-        hipStream_t st = (hipStream_t)copy_stream;
-        {
-            ProfScope p("prefetch_layer_copy", st);
-            ECF_HIP_CHECK(hipMemcpyAsync(d_buf, h_layer_blob, bytes, hipMemcpyHostToDevice, st));
+        if (n_copied)
+            *n_copied = 0;
+        if (n_missing)
+            *n_missing = 0;
+        if (!c || layer < 0 || layer >= c->L)
+            return set_error(ECF_EINVAL, "prefetch_layer: bad cache or layer");
+        if (c->h_pool.empty())
+            return set_error(ECF_EINVAL, "prefetch_layer: the cache has no host pool");
+        if (blob_bytes == 0 || blob_bytes > c->slot_bytes)
+            return set_error(ECF_EINVAL, "prefetch_layer: blob_bytes %zu not in [1, slot bytes %zu]", blob_bytes,
+                             c->slot_bytes);
+        hipStream_t cs = (hipStream_t)copy_stream;
+        for (const auto &p : c->prefetched)
+            if (p.layer == layer) {  // already pending: nothing to add
+                if (n_missing)
+                    *n_missing = p.missing;
+                if (done_event)
+                    ECF_HIP_CHECK(hipEventRecord((hipEvent_t)done_event, cs));
+                return ECF_OK;
+            }
+        hipEvent_t ev = nullptr;
+        if (!c->spare_events.empty()) {
+            ev = c->spare_events.back();
+            c->spare_events.pop_back();
+        } else {
+            ECF_HIP_CHECK(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
         }
+        const int E = c->E;
+        c->prefetched.emplace_back();
+        ecf_cache::Prefetch &pf = c->prefetched.back();
+        pf.layer = layer;
+        pf.done = ev;
+        // hold the layer's resident entries first, so no bind below evicts them
+        for (int e = 0; e < E; ++e) {
+            const int32_t sl = c->slot_of[(size_t)layer * E + e];
+            if (sl >= 0) {
+                c->held[sl] = 1;
+                pf.slots.push_back(sl);
+            }
+        }
+        int32_t budget = cache_available(c) - c->reserve;
+        // ascending expert id: a resident entry is touched (most recent), a
+        // missing one is bound while the budget lasts
+        std::vector<int32_t> bexp, bslot;
+        bool evicted = false;
+        int32_t missing = 0;
+        for (int e = 0; e < E; ++e) {
+            const int32_t sl = c->slot_of[(size_t)layer * E + e];
+            if (sl >= 0) {
+                cache_touch(c, sl);
+                continue;
+            }
+            if (budget <= 0) {
+                ++missing;
+                continue;
+            }
+            int32_t victim = -1;
+            const int32_t ns = cache_bind(c, layer, e, &victim);
+            if (ns < 0) {  // cannot happen: the budget counts bindable slots
+                ++missing;
+                continue;
+            }
+            --budget;
+            evicted |= victim >= 0;
+            c->held[ns] = 1;
+            pf.slots.push_back(ns);
+            bexp.push_back(e);
+            bslot.push_back(ns);
+        }
+        pf.missing = missing;
+        c->reserve += missing;
+        // a slot taken from another entry may still be read by queued kernels
+        if (evicted && c->have_last_compute)
+            ECF_HIP_CHECK(hipStreamWaitEvent(cs, c->last_compute, 0));
+        {
+            ProfScope p("prefetch_layer_copy", cs);
+            // runs of consecutive slots fed by consecutive host blobs go as one copy
+            const bool packed = blob_bytes == c->slot_bytes;
+            for (size_t i = 0; i < bexp.size();) {
+                size_t j = i + 1;
+                const char *h0 = (const char *)c->h_pool[(size_t)layer * E + bexp[i]];
+                while (packed && j < bexp.size() && bslot[j] == bslot[j - 1] + 1 &&
+                       (const char *)c->h_pool[(size_t)layer * E + bexp[j]] == h0 + (j - i) * blob_bytes)
+                    ++j;
+                const size_t bytes = (j - i - 1) * c->slot_bytes + blob_bytes;
+                ECF_HIP_CHECK(hipMemcpyAsync(c->d_slots + (size_t)bslot[i] * c->slot_bytes, h0, bytes,
+                                             hipMemcpyHostToDevice, cs));
+                i = j;
+            }
+        }
+        ECF_HIP_CHECK(hipEventRecord(ev, cs));
         if (done_event)
-            ECF_HIP_CHECK(hipEventRecord((hipEvent_t)done_event, st));
+            ECF_HIP_CHECK(hipEventRecord((hipEvent_t)done_event, cs));
+        if (n_copied)
+            *n_copied = (int32_t)bexp.size();
+        if (n_missing)
+            *n_missing = missing;
         return ECF_OK;
     });
 }
@@ -365,14 +463,37 @@ static int pick_path(const ecf_layer_args *a, int32_t T)
     return (T <= 64 || a->shape.inter % 128) ? ECF_PATH_DECODE : ECF_PATH_PREFILL;
 }
 
+// The expert kernels of one layer on the experts `ex` lists (0 = skipped).
+static int launch_experts(const ecf_shape &s, const ExpertTables &ex, const RouteOut &ro, const void *d_x,
+                          int32_t T, const WsLayout &wl, char *ws, int path, hipStream_t stream)
+{
+    int rc;
+    if (path == ECF_PATH_DECODE) {
+        if ((rc = launch_decode_gateup(s, ex, ro, d_x, T, (float *)(ws + wl.hbuf), stream)) ||
+            (rc = launch_decode_down(s, ex, ro, (const float *)(ws + wl.hbuf), T, (float *)(ws + wl.ybuf),
+                                     stream)))
+            return rc;
+    } else {
+        if ((rc = launch_prefill_gemm1(s, ex, ro, d_x, T, (uint16_t *)(ws + wl.hbuf), stream)) ||
+            (rc = launch_prefill_gemm2(s, ex, ro, (const uint16_t *)(ws + wl.hbuf), T, (float *)(ws + wl.ybuf),
+                                       stream)))
+            return rc;
+    }
+    return ECF_OK;
+}
+
 // Expert-cache placement for one layer-step: read the routing back, look the
 // step's experts up, split the misses by q*, bind and fill slots for the
-// copied ones, and queue the GPU work; the host-assigned experts are then
-// evaluated on the cache's threads and their partial sum is queued for the
-// combine.  Returns the device address of the host partial (or NULL).
+// copied ones, and queue the GPU work -- the hits' kernels first, the copied
+// experts' kernels once their copies have landed; the host-assigned experts
+// are then evaluated on the cache's threads and their partial sum is queued
+// for the combine.  On the prefill path every miss is copied (the grouped
+// GEMM rounds h to bf16, the host experts do not, so a split would make the
+// output depend on it).  Writes the combine's expert table (hits and copied
+// misses) and the device address of the host partial (or NULL).
 static int cache_step(const ecf_layer_args *a, const void *d_x, int32_t T, const RouteOut &ro,
                       const WsLayout &wl, char *ws, const BlobLayout &lay, int path, ecf_step_stats *st,
-                      const float **host_part_out)
+                      const uint64_t **gpu_table, const float **host_part_out)
 {
     ecf_cache *c = a->cache;
     const ecf_shape &s = a->shape;
@@ -391,21 +512,31 @@ static int cache_step(const ecf_layer_args *a, const void *d_x, int32_t T, const
     int rc;
     if ((rc = staging(c->st_counts, 4 * (size_t)E)) || (rc = staging(c->st_idx, 4 * (size_t)R)) ||
         (rc = staging(c->st_gate, 4 * (size_t)R)) || (rc = staging(c->st_x, abytes * (size_t)T * d)) ||
-        (rc = staging(c->st_out, 4 * (size_t)T * d)) || (rc = staging(c->st_ptrs, 8 * (size_t)E)) ||
+        (rc = staging(c->st_out, 4 * (size_t)T * d)) || (rc = staging(c->st_ptrs, 3 * 8 * (size_t)E)) ||
         (rc = staging(c->st_y, 4 * (size_t)R * d)))
         return rc;
     if (!c->copy_done)
         ECF_HIP_CHECK(hipEventCreateWithFlags(&c->copy_done, hipEventDisableTiming));
+    if (!c->last_compute)
+        ECF_HIP_CHECK(hipEventCreateWithFlags(&c->last_compute, hipEventDisableTiming));
     if (!c->pool) {
         int n = c->host_threads > 0 ? c->host_threads : (int)std::min(16u, std::max(1u, std::thread::hardware_concurrency()));
         c->pool = new HostPool(n);
     }
+    // a pending whole-layer prefetch of this layer: its hold ends here, and its
+    // copies must land before any kernel reads the layer's slots
+    struct PrefetchWait {
+        ecf_cache *c;
+        hipEvent_t ev;
+        ~PrefetchWait() { cache_spare_event(c, ev); }
+    } pf{c, cache_take_prefetch(c, a->layer)};
     int32_t *h_counts = (int32_t *)c->st_counts.p, *h_idx = (int32_t *)c->st_idx.p;
     float *h_gate = (float *)c->st_gate.p;
     ECF_HIP_CHECK(hipMemcpyAsync(h_counts, ro.counts, 4 * (size_t)E, hipMemcpyDeviceToHost, stream));
     ECF_HIP_CHECK(hipMemcpyAsync(h_idx, ro.idx, 4 * (size_t)R, hipMemcpyDeviceToHost, stream));
     ECF_HIP_CHECK(hipMemcpyAsync(h_gate, ro.gate, 4 * (size_t)R, hipMemcpyDeviceToHost, stream));
-    ECF_HIP_CHECK(hipMemcpyAsync(c->st_x.p, d_x, abytes * (size_t)T * d, hipMemcpyDeviceToHost, stream));
+    if (path == ECF_PATH_DECODE)
+        ECF_HIP_CHECK(hipMemcpyAsync(c->st_x.p, d_x, abytes * (size_t)T * d, hipMemcpyDeviceToHost, stream));
     const auto t0 = std::chrono::steady_clock::now();
     ECF_HIP_CHECK(hipStreamSynchronize(stream));
     const auto t1 = std::chrono::steady_clock::now();
@@ -423,16 +554,24 @@ static int cache_step(const ecf_layer_args *a, const void *d_x, int32_t T, const
             miss.push_back(U[i]);
     const int32_t m = (int32_t)miss.size();
     int32_t q;
-    switch (a->q_mode) {
-    case ECF_Q_ALL_GPU: q = m; break;
-    case ECF_Q_ALL_HOST: q = 0; break;
-    case ECF_Q_FIXED: q = std::min(std::max(a->q_fixed, 0), m); break;
-    default:
-        q = qstar_split(m, a->b_p, a->b_h);
-        if (q < 0)
-            return q;
+    if (path == ECF_PATH_PREFILL) {
+        q = m;
+        if (q > ecf_cache_available(c))
+            return set_error(ECF_ENOSPC,
+                             "cache mode, prefill path: %d missed experts to copy, %d slots available", q,
+                             ecf_cache_available(c));
+    } else {
+        switch (a->q_mode) {
+        case ECF_Q_ALL_GPU: q = m; break;
+        case ECF_Q_ALL_HOST: q = 0; break;
+        case ECF_Q_FIXED: q = std::min(std::max(a->q_fixed, 0), m); break;
+        default:
+            q = qstar_split(m, a->b_p, a->b_h);
+            if (q < 0)
+                return q;
+        }
+        q = std::min(q, ecf_cache_available(c));
     }
-    q = std::min(q, ecf_cache_available(c));
     // misses to copy first: most routed rows, then lower id
     std::stable_sort(miss.begin(), miss.end(),
                      [&](int32_t x, int32_t y) { return h_counts[x] > h_counts[y]; });
@@ -440,38 +579,45 @@ static int cache_step(const ecf_layer_args *a, const void *d_x, int32_t T, const
     if ((rc = expert_cache_evict(c, a->layer, miss.data(), q, copy_slots.data(), nullptr)) != ECF_OK)
         return rc;
 
-    uint64_t *h_ptrs = (uint64_t *)c->st_ptrs.p;
-    std::memset(h_ptrs, 0, 8 * (size_t)E);
+    // three expert tables: hits, copied misses, and both (for the combine)
+    uint64_t *h_hit = (uint64_t *)c->st_ptrs.p, *h_cp = h_hit + E, *h_all = h_cp + E;
+    std::memset(h_hit, 0, 3 * 8 * (size_t)E);
     for (size_t i = 0; i < U.size(); ++i)
         if (slots[i] >= 0)
-            h_ptrs[U[i]] = (uint64_t)(c->d_slots + (size_t)slots[i] * c->slot_bytes);
+            h_all[U[i]] = h_hit[U[i]] = (uint64_t)(c->d_slots + (size_t)slots[i] * c->slot_bytes);
     int64_t bytes_h2d = 0;
     for (int32_t i = 0; i < q; ++i) {
         char *dst = c->d_slots + (size_t)copy_slots[i] * c->slot_bytes;
-        h_ptrs[miss[i]] = (uint64_t)dst;
+        h_all[miss[i]] = h_cp[miss[i]] = (uint64_t)dst;
         const void *src = c->h_pool[(size_t)a->layer * E + miss[i]];
         ProfScope p("slot_fill_copy", cstream);
         ECF_HIP_CHECK(hipMemcpyAsync(dst, src, lay.bytes, hipMemcpyHostToDevice, cstream));
         bytes_h2d += (int64_t)lay.bytes;
     }
-    uint64_t *d_ptrs = (uint64_t *)(ws + wl.ptrs);
-    ECF_HIP_CHECK(hipMemcpyAsync(d_ptrs, h_ptrs, 8 * (size_t)E, hipMemcpyHostToDevice, stream));
+    uint64_t *d_tabs = (uint64_t *)(ws + wl.ptrs);  // [3][E]
+    ECF_HIP_CHECK(hipMemcpyAsync(d_tabs, h_hit, 3 * 8 * (size_t)E, hipMemcpyHostToDevice, stream));
+    if (pf.ev)
+        ECF_HIP_CHECK(hipStreamWaitEvent(stream, pf.ev, 0));
+    const bool split_launch = q > 0 && cstream != stream && (int32_t)U.size() > m;
+    if (split_launch) {  // the hits' kernels run while the copies are in flight
+        if ((rc = launch_experts(s, ExpertTables{d_tabs, lay}, ro, d_x, T, wl, ws, path, stream)) != ECF_OK)
+            return rc;
+    }
     if (q > 0 && cstream != stream) {
         ECF_HIP_CHECK(hipEventRecord(c->copy_done, cstream));
         ECF_HIP_CHECK(hipStreamWaitEvent(stream, c->copy_done, 0));
     }
-    ExpertTables ex{d_ptrs, lay};
-    if (path == ECF_PATH_DECODE) {
-        if ((rc = launch_decode_gateup(s, ex, ro, d_x, T, (float *)(ws + wl.hbuf), stream)) ||
-            (rc = launch_decode_down(s, ex, ro, (const float *)(ws + wl.hbuf), T, (float *)(ws + wl.ybuf),
-                                     stream)))
-            return rc;
-    } else {
-        if ((rc = launch_prefill_gemm1(s, ex, ro, d_x, T, (uint16_t *)(ws + wl.hbuf), stream)) ||
-            (rc = launch_prefill_gemm2(s, ex, ro, (const uint16_t *)(ws + wl.hbuf), T, (float *)(ws + wl.ybuf),
-                                       stream)))
-            return rc;
-    }
+    const uint64_t *tab = split_launch ? d_tabs + E : d_tabs + 2 * E;
+    if ((rc = launch_experts(s, ExpertTables{tab, lay}, ro, d_x, T, wl, ws, path, stream)) != ECF_OK)
+        return rc;
+    // no later copy may overwrite a slot these kernels read until they are done
+    ECF_HIP_CHECK(hipEventRecord(c->last_compute, stream));
+    c->have_last_compute = true;
+    *gpu_table = d_tabs + 2 * E;
+    // the forward call's layer-step ends here: its pins are released
+    ++c->gen;
+    c->n_pinned = 0;
+    c->step_layer = -1;
 
     // host experts (the m - q misses not copied), in parallel with the GPU
     std::vector<HostExpertJob> jobs;
@@ -569,10 +715,6 @@ int forward_impl(const ecf_layer_args *a, const void *d_x, int32_t T, float *d_o
         const int path = pick_path(a, T);
         if (path == ECF_PATH_PREFILL && (s.w_dtype == ECF_F32 || s.inter % 128))
             return set_error(ECF_EUNSUPPORTED, "the prefill path needs bf16/MXFP4 weights and inter %% 128 == 0");
-        if (path == ECF_PATH_PREFILL && a->cache)
-            return set_error(ECF_EUNSUPPORTED,
-                             "cache mode runs the decode GEMVs (the prefill GEMM's bf16 h would make the "
-                             "output depend on the split)");
         hipStream_t stream = (hipStream_t)a->stream;
         char *ws = (char *)d_ws;
         BlobLayout lay;
@@ -605,19 +747,12 @@ int forward_impl(const ecf_layer_args *a, const void *d_x, int32_t T, float *d_o
         const float *host_part = nullptr;
         ExpertTables ex{a->d_expert_ptrs, lay};
         if (a->cache) {
-            if ((rc = cache_step(a, d_x, T, ro, wl, ws, lay, path, stats, &host_part)) != ECF_OK)
+            const uint64_t *tab = nullptr;
+            if ((rc = cache_step(a, d_x, T, ro, wl, ws, lay, path, stats, &tab, &host_part)) != ECF_OK)
                 return rc;
-            ex.ptrs = (const uint64_t *)(ws + wl.ptrs);
-        } else if (path == ECF_PATH_DECODE) {
-            if ((rc = launch_decode_gateup(s, ex, ro, d_x, T, (float *)(ws + wl.hbuf), stream)) ||
-                (rc = launch_decode_down(s, ex, ro, (const float *)(ws + wl.hbuf), T, (float *)(ws + wl.ybuf),
-                                         stream)))
-                return rc;
-        } else {
-            if ((rc = launch_prefill_gemm1(s, ex, ro, d_x, T, (uint16_t *)(ws + wl.hbuf), stream)) ||
-                (rc = launch_prefill_gemm2(s, ex, ro, (const uint16_t *)(ws + wl.hbuf), T,
-                                           (float *)(ws + wl.ybuf), stream)))
-                return rc;
+            ex.ptrs = tab;
+        } else if ((rc = launch_experts(s, ex, ro, d_x, T, wl, ws, path, stream)) != ECF_OK) {
+            return rc;
         }
         if ((rc = launch_combine(s, ex, ro, (const float *)(ws + wl.ybuf), T, a->d_residual, host_part, d_out,
                                  a->d_out_act, stream)) != ECF_OK)

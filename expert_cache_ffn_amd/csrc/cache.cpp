@@ -13,7 +13,12 @@
 // given (ascending expert id from the forward call); a bind takes the lowest
 // free slot, else the least recently used entry not used by the current
 // layer-step; entries of the current layer-step are pinned until the next
-// lookup opens a new one.
+// lookup opens a new one.  A whole-layer prefetch (explainer section "Prefill:
+// full-layer double buffer and semantic anchors": the next layer streams into
+// the same slot pool while the current one computes) holds its layer's
+// entries until that layer's forward call; held entries are never evicted,
+// and the experts a prefetch could not place stay reserved: a later prefetch
+// leaves that many slots, so that forward call can still fill them on demand.
 #include <memory>
 
 #include "cache_internal.h"
@@ -49,7 +54,78 @@ void push_mru(ecf_cache *c, int32_t s)
 }
 
 bool pinned(const ecf_cache *c, int32_t s) { return c->pin_gen[s] == c->gen; }
+bool evictable(const ecf_cache *c, int32_t s) { return !pinned(c, s) && !c->held[s]; }
 }  // namespace
+
+namespace ecf {
+
+int32_t cache_available(const ecf_cache *c)
+{
+    int32_t blocked = c->n_pinned;  // resident slots no bind may take
+    for (const auto &p : c->prefetched)
+        for (int32_t s : p.slots)
+            blocked += pinned(c, s) ? 0 : 1;
+    return (int32_t)c->free.size() + (c->n_resident - blocked);
+}
+
+void cache_touch(ecf_cache *c, int32_t s)
+{
+    unlink(c, s);
+    push_mru(c, s);
+}
+
+int32_t cache_bind(ecf_cache *c, int32_t layer, int32_t expert, int32_t *victim)
+{
+    int32_t s;
+    *victim = -1;
+    if (!c->free.empty()) {
+        s = *c->free.begin();
+        c->free.erase(c->free.begin());
+    } else {
+        s = c->head;
+        while (s >= 0 && !evictable(c, s))
+            s = c->next[s];
+        if (s < 0)
+            return -1;
+        const int64_t old = c->key_of_slot[s];
+        c->slot_of[old] = -1;
+        unlink(c, s);
+        --c->n_resident;
+        *victim = (int32_t)old;
+        ++c->stats.evictions;
+    }
+    const int64_t key = key_of(c, layer, expert);
+    c->slot_of[key] = s;
+    c->key_of_slot[s] = key;
+    push_mru(c, s);
+    ++c->n_resident;
+    ++c->stats.inserts;
+    return s;
+}
+
+hipEvent_t cache_take_prefetch(ecf_cache *c, int32_t layer)
+{
+    for (size_t i = 0; i < c->prefetched.size(); ++i) {
+        auto &p = c->prefetched[i];
+        if (p.layer != layer)
+            continue;
+        for (int32_t s : p.slots)
+            c->held[s] = 0;
+        c->reserve -= p.missing;
+        hipEvent_t ev = p.done;
+        c->prefetched.erase(c->prefetched.begin() + i);
+        return ev;
+    }
+    return nullptr;
+}
+
+void cache_spare_event(ecf_cache *c, hipEvent_t ev)
+{
+    if (ev)
+        c->spare_events.push_back(ev);
+}
+
+}  // namespace ecf
 
 extern "C" {
 
@@ -75,6 +151,7 @@ int ecf_cache_create(int32_t n_layers, int32_t n_experts, int32_t n_slots, int32
         c->prev.assign(max_slots, -1);
         c->next.assign(max_slots, -1);
         c->pin_gen.assign(max_slots, 0);
+        c->held.assign(max_slots, 0);
         for (int32_t s = 0; s < n_slots; ++s)
             c->free.insert(s);
         c->host_threads = host_threads;
@@ -113,8 +190,7 @@ int expert_cache_lookup(ecf_cache *c, int32_t layer, const int32_t *experts, int
                 continue;
             }
             ++c->stats.hits;
-            unlink(c, s);
-            push_mru(c, s);
+            ecf::cache_touch(c, s);
             if (!pinned(c, s)) {
                 c->pin_gen[s] = c->gen;
                 ++c->n_pinned;
@@ -128,7 +204,7 @@ int32_t ecf_cache_available(const ecf_cache *c)
 {
     if (!c)
         return set_error(ECF_EINVAL, "ecf_cache_available: NULL cache");
-    return (int32_t)c->free.size() + (c->n_resident - c->n_pinned);
+    return ecf::cache_available(c);
 }
 
 int expert_cache_evict(ecf_cache *c, int32_t layer, const int32_t *experts, int32_t n, int32_t *slots,
@@ -153,31 +229,12 @@ int expert_cache_evict(ecf_cache *c, int32_t layer, const int32_t *experts, int3
             return set_error(ECF_ENOSPC, "expert_cache_evict: %d slots wanted, %d available", n,
                              ecf_cache_available(c));
         for (int32_t i = 0; i < n; ++i) {
-            int32_t s, victim = -1;
-            if (!c->free.empty()) {
-                s = *c->free.begin();
-                c->free.erase(c->free.begin());
-            } else {
-                s = c->head;
-                while (s >= 0 && pinned(c, s))
-                    s = c->next[s];
-                if (s < 0)  // cannot happen: availability was checked
-                    return set_error(ECF_ESTATE, "expert_cache_evict: no evictable slot");
-                const int64_t old = c->key_of_slot[s];
-                c->slot_of[old] = -1;
-                unlink(c, s);
-                --c->n_resident;
-                victim = (int32_t)old;
-                ++c->stats.evictions;
-            }
-            const int64_t key = key_of(c, layer, experts[i]);
-            c->slot_of[key] = s;
-            c->key_of_slot[s] = key;
-            push_mru(c, s);
-            ++c->n_resident;
+            int32_t victim = -1;
+            const int32_t s = ecf::cache_bind(c, layer, experts[i], &victim);
+            if (s < 0)  // cannot happen: availability was checked
+                return set_error(ECF_ESTATE, "expert_cache_evict: no evictable slot");
             c->pin_gen[s] = c->gen;
             ++c->n_pinned;
-            ++c->stats.inserts;
             slots[i] = s;
             if (victims)
                 victims[i] = victim;
@@ -208,6 +265,13 @@ int ecf_cache_resize(ecf_cache *c, int32_t n_slots)
     return ::ecf::guarded("ecf_cache_resize", [&]() -> int {
         if (!c || n_slots < 0 || n_slots > c->max_slots)
             return set_error(ECF_EINVAL, "ecf_cache_resize: n_slots must be in [0, max_slots]");
+        // a safe point: pending prefetch copies land first, and their holds end
+        while (!c->prefetched.empty()) {
+            hipEvent_t ev = ecf::cache_take_prefetch(c, c->prefetched.front().layer);
+            if (ev && hipEventSynchronize(ev) != hipSuccess)
+                return set_error(ECF_EHIP, "ecf_cache_resize: waiting for a prefetch failed");
+            ecf::cache_spare_event(c, ev);
+        }
         for (int32_t s = n_slots; s < c->n_slots; ++s) {
             c->free.erase(s);
             const int64_t key = c->key_of_slot[s];

@@ -22,6 +22,21 @@ struct ecf_cache {
     uint32_t gen = 1;
     int32_t n_resident = 0, n_pinned = 0;
     int32_t step_layer = -1;           // layer of the open layer-step, -1 if none
+    // Whole-layer prefetches not yet consumed by that layer's forward call:
+    // their resident entries are held (no bind evicts them) and `missing` of
+    // the layer's experts did not fit; `reserve` (the sum of those) is what
+    // a later prefetch leaves for those forward calls to fill on demand.
+    struct Prefetch {
+        int32_t layer = -1, missing = 0;
+        std::vector<int32_t> slots;    // held slots
+        hipEvent_t done = nullptr;     // recorded on the copy stream after the layer's copies
+    };
+    std::vector<Prefetch> prefetched;
+    std::vector<char> held;            // [max_slots] 1 while held by a prefetch
+    int32_t reserve = 0;
+    std::vector<hipEvent_t> spare_events;
+    hipEvent_t last_compute = nullptr; // recorded after each cache-mode forward's kernels
+    bool have_last_compute = false;
     ecf_cache_stats stats{};
     int32_t host_threads = 0;
     // forward-call host resources, created on first use
@@ -34,6 +49,20 @@ struct ecf_cache {
 };
 
 namespace ecf {
+// Slots a bind could take now: free ones plus resident entries neither pinned
+// by the open layer-step nor held by a prefetch.
+int32_t cache_available(const ecf_cache *c);
+// Bind (layer, expert) to the lowest free slot, else to the least recently used
+// evictable entry (evicted; its key -> *victim, else -1).  Becomes MRU.  The
+// caller has checked availability.  Returns the slot, or -1 if none.
+int32_t cache_bind(ecf_cache *c, int32_t layer, int32_t expert, int32_t *victim);
+// Move a resident slot to the most recently used end.
+void cache_touch(ecf_cache *c, int32_t slot);
+// End the hold of `layer`'s pending prefetch (if any): returns its copy event
+// (the caller's compute stream must wait on it before reading the layer's
+// slots, then give it back with cache_spare_event) or nullptr.
+hipEvent_t cache_take_prefetch(ecf_cache *c, int32_t layer);
+void cache_spare_event(ecf_cache *c, hipEvent_t ev);
 // Grow a pinned host staging buffer to at least `bytes` (hipHostMalloc).
 int staging(ecf_cache::Staging &s, size_t bytes);
 void cache_release_host(ecf_cache *c);

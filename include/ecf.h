@@ -149,7 +149,8 @@ int expert_cache_lookup(ecf_cache *cache, int32_t layer, const int32_t *experts,
 int expert_cache_evict(ecf_cache *cache, int32_t layer, const int32_t *experts, int32_t n,
                        int32_t *slots, int32_t *victims);
 
-/* Slots a bind in the current layer-step could still take (free + unpinned). */
+/* Slots a bind could take now: free ones, plus resident entries neither pinned
+ * by the open layer-step nor held by a pending prefetch. */
 int32_t ecf_cache_available(const ecf_cache *cache);
 /* Resident slot of (layer, expert) or -1; does not touch the LRU order. */
 int32_t ecf_cache_slot_of(const ecf_cache *cache, int32_t layer, int32_t expert);
@@ -163,15 +164,35 @@ int ecf_cache_get_stats(const ecf_cache *cache, ecf_cache_stats *out);
  */
 int ecf_cache_resize(ecf_cache *cache, int32_t n_slots);
 
-/* ---- prefill layer prefetch [PL "Prefill: full-layer double buffer ..."] ------
- * Queue one copy of a whole layer's expert blobs (bytes, contiguous, pinned
- * host) into d_buf on copy_stream, then record done_event (nullable) on it.
- * The copy does not depend on routing, so it may start before the layer's
- * router has run.  Asynchronous; returns once queued.  ECF_ENOSPC if
- * buf_capacity < bytes (the caller then falls back to on-demand copies).
+/* ---- prefill layer prefetch [PL "Prefill: full-layer double buffer and semantic
+ *      anchors": layer l+1 streams into the same slot pool while layer l computes,
+ *      and what is left of it afterwards warms the decode cache] -------------------
+ * Queue the copy of every expert of `layer` into the cache's slots, on
+ * copy_stream, before that layer's routing is known.  In ascending expert id,
+ * an entry already resident becomes most recently used, and a missing one is
+ * bound like a miss (lowest free slot, else the least recently used entry
+ * neither pinned nor held) and becomes most recently used; its host blob
+ * (blob_bytes <= the slot size, from the cache's host pool) is copied into the
+ * slot.  Runs of consecutive slots fed by consecutive host blobs (slot size ==
+ * blob_bytes) go as one copy, so a layer stored contiguously on the host
+ * streams as a few large copies.  Copies into a slot taken from another entry
+ * wait first for the kernels of the last cache-mode forward call (call this
+ * before the forward call of the layer now computing, then the two overlap).
+ * The layer's entries are then held: no bind evicts them until the forward
+ * call of `layer`, which waits on device for these copies and ends the hold.
+ * If the layer does not fit, the experts that do are placed (ascending id)
+ * and the rest, *n_missing of them, are reserved: a later prefetch places at
+ * most the available slots less every pending reserve, so the forward calls of
+ * the held layers, taken in prefetch order, can still fill their missing
+ * experts on demand.  *n_copied receives the
+ * experts copied (both outputs nullable).  done_event (nullable) is recorded
+ * on copy_stream after the copies.  A second prefetch of a pending layer adds
+ * nothing.  Asynchronous; returns once queued.  ECF_EINVAL for bad arguments
+ * or a cache without a host pool; ECF_EHIP on a HIP failure (the cache's
+ * contents are then undefined).
  */
-int prefetch_layer(const void *h_layer_blob, void *d_buf, size_t bytes, size_t buf_capacity,
-                   void *copy_stream, void *done_event);
+int prefetch_layer(ecf_cache *cache, int32_t layer, size_t blob_bytes, void *copy_stream,
+                   void *done_event, int32_t *n_copied, int32_t *n_missing);
 
 /* ---- one layer forward --------------------------------------------------------- */
 enum { ECF_Q_AUTO = 0, ECF_Q_ALL_GPU = 1, ECF_Q_ALL_HOST = 2, ECF_Q_FIXED = 3 };
@@ -206,10 +227,13 @@ typedef struct {
     int32_t path;                /* ECF_PATH_*: AUTO takes the decode GEMVs in cache mode, for
                                     fp32 weights and, for bf16 / MXFP4, while T <= 64 or
                                     I % 128 != 0; the prefill grouped GEMM otherwise (bf16 /
-                                    MXFP4, all-resident only: it rounds h to bf16, the host
-                                    experts do not, so cache mode + PREFILL is
-                                    ECF_EUNSUPPORTED; it also needs x and one expert
-                                    blob each under 4 GiB, else ECF_EUNSUPPORTED) */
+                                    MXFP4; it needs I % 128 == 0 and x and one expert blob
+                                    each under 4 GiB, else ECF_EUNSUPPORTED).  In cache mode
+                                    PREFILL copies every miss into a slot and computes none
+                                    on the host (the GEMM rounds h to bf16, the host experts
+                                    do not, so a split would change the output); q_mode is
+                                    then ignored and too few slots for the misses is
+                                    ECF_ENOSPC */
     /* buffers */
     void *d_ws;                  /* workspace, >= ecf_workspace_bytes(shape, T) bytes, 256-B aligned */
     size_t ws_bytes;
@@ -231,8 +255,12 @@ typedef struct {
  * in a_dtype (16-byte aligned, else ECF_EINVAL), out [T][d] fp32.  All-resident mode is fully asynchronous on
  * args->stream.  Cache mode blocks the calling thread once on the routing
  * readback (the q* decision is taken on the host from the step's miss count
- * [TF "Bandwidth-adaptive execution (q* policy)"]), computes host-assigned
- * experts on the cache's host threads, and returns with the rest queued.
+ * [TF "Bandwidth-adaptive execution (q* policy)"]), queues the kernels of the
+ * hits, then those of the copied misses behind their copies, computes
+ * host-assigned experts on the cache's host threads, and returns with the rest
+ * queued.  A cache-mode call opens and closes its own layer-step (its pins end
+ * when it returns), ends the hold of a pending prefetch of its layer, and must
+ * use one compute stream for all calls on a cache.
  * n_tokens == 0 is a no-op; n_tokens * top_k above 2^26 is ECF_EINVAL (row
  * indices are 32-bit).  stats (nullable) receives the step's figures.
  */

@@ -271,9 +271,24 @@ class LRURef:
       * the misses to copy are the first q of the misses ordered by
         (routed rows descending, expert id ascending);
       * a copied miss takes the lowest free slot, else the slot of the least
-        recently used entry that this layer-step does not use;
+        recently used entry that this layer-step does not use and no pending
+        prefetch holds;
       * misses computed on the host are not inserted;
-      * q is cut to the slots that can be had (free + not used this step).
+      * q is cut to the slots that can be had (see available());
+      * on the prefill path every miss is copied (q = m), and more misses
+        than available slots is an error.
+
+    Whole-layer prefetch (FreeToken paper explainer, "Prefill: full-layer
+    double buffer and semantic anchors": the next layer streams into the slot
+    pool while the current one computes, and what stays resident warms
+    decode), with the readings taken for it:
+      * in ascending expert id, a resident entry is touched and a missing one
+        is inserted (most recent) while slots can be had;
+      * the layer's resident entries are then held -- no insertion evicts
+        them -- until that layer's next step, which ends the hold first;
+      * the experts that did not fit are counted as reserved: a later
+        prefetch places at most available() minus the reserve, so the held
+        layers' steps can still copy them.
     """
 
     def __init__(self, n_slots: int, n_experts: int):
@@ -281,13 +296,63 @@ class LRURef:
         self.E = n_experts
         self.od: "OrderedDict[tuple, int]" = OrderedDict()
         self.free = list(range(n_slots))
+        self.held = {}  # layer -> [set of held keys, experts that did not fit]
+        self.reserve = 0
         self.stats = dict(lookups=0, hits=0, misses=0, inserts=0, evictions=0)
 
     def resident(self, layer: int, expert: int):
         return self.od.get((layer, expert))
 
-    def step(self, layer: int, rows: dict, q_of_m):
+    def _held_keys(self):
+        return set().union(*(h[0] for h in self.held.values())) if self.held else set()
+
+    def available(self, pinned=frozenset()) -> int:
+        """Free slots plus entries neither pinned by the step nor held."""
+        held = self._held_keys()
+        return len(self.free) + sum(1 for key, s in self.od.items() if s not in pinned and key not in held)
+
+    def _insert(self, key, pinned=frozenset()):
+        """Lowest free slot, else the least recently used entry neither pinned nor held."""
+        if self.free:
+            s = min(self.free)
+            self.free.remove(s)
+            victim = None
+        else:
+            held = self._held_keys()
+            victim = next(k for k, sl in self.od.items() if sl not in pinned and k not in held)
+            s = self.od.pop(victim)
+            self.stats["evictions"] += 1
+        self.od[key] = s
+        self.stats["inserts"] += 1
+        return s, victim
+
+    def prefetch(self, layer: int):
+        """Whole-layer prefetch; returns {copied: [experts], missing: count}."""
+        if layer in self.held:
+            return dict(copied=[], missing=self.held[layer][1])
+        keys = {(layer, e) for e in range(self.E) if (layer, e) in self.od}
+        self.held[layer] = [keys, 0]
+        budget = self.available() - self.reserve
+        copied, missing = [], 0
+        for e in range(self.E):
+            key = (layer, e)
+            if key in self.od:
+                self.od.move_to_end(key)
+            elif budget > 0:
+                self._insert(key)
+                keys.add(key)
+                copied.append(e)
+                budget -= 1
+            else:
+                missing += 1
+        self.held[layer][1] = missing
+        self.reserve += missing
+        return dict(copied=copied, missing=missing)
+
+    def step(self, layer: int, rows: dict, q_of_m, prefill: bool = False):
         """rows: expert -> routed row count (> 0).  Returns a plan dict."""
+        if layer in self.held:
+            self.reserve -= self.held.pop(layer)[1]
         U = sorted(rows)
         pinned = set()
         hits = {}
@@ -304,30 +369,27 @@ class LRURef:
                 hits[e] = s
                 self.stats["hits"] += 1
         m = len(misses)
-        q = q_of_m(m)
-        avail = len(self.free) + sum(1 for s in self.od.values() if s not in pinned)
-        q = min(q, avail)
+        avail = self.available(pinned)
+        if prefill:
+            q = m
+            if q > avail:
+                raise ValueError(f"prefill step: {q} misses, {avail} slots available")
+        else:
+            q = min(q_of_m(m), avail)
         order = sorted(misses, key=lambda e: (-rows[e], e))
         copied, victims = {}, {}
         for e in order[:q]:
-            if self.free:
-                s = min(self.free)
-                self.free.remove(s)
-                victims[e] = None
-            else:
-                vk = next(key for key, sl in self.od.items() if sl not in pinned)
-                s = self.od.pop(vk)
-                victims[e] = vk
-                self.stats["evictions"] += 1
-            self.od[(layer, e)] = s
+            s, victims[e] = self._insert((layer, e), pinned)
             pinned.add(s)
             copied[e] = s
-            self.stats["inserts"] += 1
         host = order[q:]
         return dict(hits=hits, copied=copied, host=host, victims=victims, m=m, q=q)
 
     def resize(self, n_slots: int):
-        """Keep the entries in slots below n_slots (slot memory is fixed per id)."""
+        """Keep the entries in slots below n_slots (slot memory is fixed per id);
+        pending prefetch holds end (a resize is a safe point)."""
+        self.held.clear()
+        self.reserve = 0
         for key, s in list(self.od.items()):
             if s >= n_slots:
                 del self.od[key]

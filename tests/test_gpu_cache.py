@@ -1,7 +1,8 @@
 """GPU tests of the expert-cache mode: split invariance (all-GPU, all-host,
 fixed and q* splits agree with the all-resident layer within 1e-5 * RMS),
 cache-state invariance (cold, warm, resized), LRU statistics against the
-oracle's reference LRU on the same routing, and prefetch_layer."""
+oracle's reference LRU on the same routing, the whole-layer prefetch into the
+slot pool and prefill through it."""
 import numpy as np
 import pytest
 import torch
@@ -95,7 +96,8 @@ def test_split_invariance_small(mode, q_fixed, w_dtype):
 def test_split_invariance_many_tokens(w_dtype):
     """100 tokens (past the decode/prefill switch of the all-resident mode): cache
     mode still runs the GEMVs, so every split agrees with the resident decode
-    path within 1e-5; an explicit PREFILL request in cache mode is refused."""
+    path within 1e-5.  An explicit PREFILL request in cache mode copies every miss
+    (no host split), so with 6 slots for ~16 routed experts it is ECF_ENOSPC."""
     cfg = syn.gen.Config(102, "cs", (100,), 512, 16, 256, 4, w_dtype, "bf16", "zipf", layers=1)
     T, d = 100, cfg.hidden
     cs = CachedSetup(cfg, 1, n_slots=6)
@@ -117,7 +119,7 @@ def test_split_invariance_many_tokens(w_dtype):
             assert err <= SPLIT_TOL
         with pytest.raises(ecf.EcfError) as ei:
             _run(lay, lay.args(router_logits=lg, cache=cs.cache, path=ecf.ECF_PATH_PREFILL), x, T, d)
-        assert ei.value.code == ecf.ECF_EUNSUPPORTED
+        assert ei.value.code == ecf.ECF_ENOSPC
     finally:
         cs.close()
 
@@ -263,19 +265,119 @@ def test_residual_stack_and_activation_copy():
         cs.close()
 
 
-def test_prefetch_layer_copies_and_signals():
-    n = 64 << 20
-    h = torch.randint(0, 255, (n,), dtype=torch.uint8).pin_memory()
-    dbuf = torch.zeros(2 * n, dtype=torch.uint8, device="cuda")
+def test_prefetch_layer_fills_slots_and_signals():
+    """prefetch_layer binds every expert of a layer to cache slots and copies each
+    host blob in (consecutive slots and host blobs as one copy); the slots then
+    hold the blobs byte for byte, a second prefetch of the pending layer adds
+    nothing, and bad arguments are refused."""
+    cfg = syn.gen.Config(104, "pf", (8,), 512, 8, 256, 2, "bf16", "bf16", "uniform", layers=2)
+    cs = CachedSetup(cfg, 2, n_slots=16)
     s = torch.cuda.Stream()
     ev = torch.cuda.Event()
     ev.record(s)  # creates the underlying hipEvent
-    ecf.prefetch_layer(h.data_ptr(), dbuf.data_ptr() + n, n, n, s.cuda_stream, ev.cuda_event)
-    ev.synchronize()
-    assert torch.equal(dbuf[n:].cpu(), h)
-    with pytest.raises(ecf.EcfError) as ei:
-        ecf.prefetch_layer(h.data_ptr(), dbuf.data_ptr(), n, n - 1, s.cuda_stream, ev.cuda_event)
-    assert ei.value.code == ecf.ECF_ENOSPC
+    try:
+        blob = ecf.ecf_expert_bytes(cs.shape)
+        assert ecf.prefetch_layer(cs.cache, 1, blob, s.cuda_stream, ev.cuda_event) == (8, 0)
+        ev.synchronize()
+        for e in range(8):
+            sl = ecf.ecf_cache_slot_of(cs.cache, 1, e)
+            assert sl == e  # lowest free slots, ascending expert id
+            assert torch.equal(cs.slots[sl].cpu(), cs.host[cs.blob_of(1, e)])
+        assert ecf.prefetch_layer(cs.cache, 1, blob, s.cuda_stream) == (0, 0)
+        with pytest.raises(ecf.EcfError) as ei:
+            ecf.prefetch_layer(cs.cache, 2, blob, s.cuda_stream)
+        assert ei.value.code == ecf.ECF_EINVAL
+        with pytest.raises(ecf.EcfError) as ei:
+            ecf.prefetch_layer(cs.cache, 0, cs.slot_bytes + 1, s.cuda_stream)
+        assert ei.value.code == ecf.ECF_EINVAL
+        assert ecf.ecf_cache_get_stats(cs.cache)["inserts"] == 8
+    finally:
+        cs.close()
+
+
+def _rows_of(lg, k):
+    idx, _ = oracle.route(lg.cpu().numpy(), k)
+    rows = {}
+    for e in idx.ravel():
+        rows[int(e)] = rows.get(int(e), 0) + 1
+    return rows
+
+
+@pytest.mark.parametrize("w_dtype,layers_of_slots", [("bf16", 2.0), ("mxfp4", 2.0), ("bf16", 1.5)])
+def test_streamed_prefill_through_slot_pool(w_dtype, layers_of_slots):
+    """Prefill over 3 stacked layers with layer l+1 prefetched into the shared slot
+    pool while layer l computes (no host sync between layers): each layer's
+    output equals the all-resident prefill layer bit for bit and the oracle
+    within the bar; with 1.5 layers of slots part of each prefetch does not fit
+    and the forward call fills the rest on demand.  Afterwards the cache state
+    (every (layer, expert) slot, the LRU counters) equals the reference LRU run
+    through the same prefetches and steps, and a decode step on the last layer
+    finds its experts resident."""
+    E, L, T, k = 16, 3, 300, 4
+    cfg = syn.gen.Config(105, "pf", (T,), 512, E, 256, k, w_dtype, "bf16", "uniform", layers=L)
+    d = cfg.hidden
+    n_slots = int(layers_of_slots * E)
+    say(f"case: streamed prefill {w_dtype}, {n_slots} slots for {E}-expert layers")
+    cs = CachedSetup(cfg, L, n_slots=n_slots)
+    lay = Layer(cs.shape, T)
+    cstream = torch.cuda.Stream()
+    ref_lru = oracle.LRURef(n_slots, E)
+    blob = ecf.ecf_expert_bytes(cs.shape)
+    tol = 5e-2 if w_dtype == "mxfp4" else 2e-2
+    try:
+        xs = [syn.activations(cfg, T, layer=l, device="cuda") for l in range(L)]
+        lgs = [syn.router_logits(cfg, T, layer=l, device="cuda") for l in range(L)]
+        outs = [torch.full((T, d), float("nan"), dtype=torch.float32, device="cuda") for _ in range(L)]
+        torch.cuda.synchronize()
+        pf = [ecf.prefetch_layer(cs.cache, 0, blob, cstream.cuda_stream)]
+        sts = []
+        for l in range(L):
+            if l + 1 < L:
+                pf.append(ecf.prefetch_layer(cs.cache, l + 1, blob, cstream.cuda_stream))
+            a = lay.args(layer=l, router_logits=lgs[l], cache=cs.cache, path=ecf.ECF_PATH_PREFILL,
+                         copy_stream=cstream)
+            sts.append(lay.forward(a, xs[l], outs[l]))
+        torch.cuda.synchronize()
+        for l in range(L):
+            r = ref_lru.prefetch(l) if l == 0 else None
+            if l + 1 < L:
+                r1 = ref_lru.prefetch(l + 1)
+                assert (len(r1["copied"]), r1["missing"]) == pf[l + 1], (l, r1, pf[l + 1])
+            if r is not None:
+                assert (len(r["copied"]), r["missing"]) == pf[0]
+            plan = ref_lru.step(l, _rows_of(lgs[l], k), lambda m: m, prefill=True)
+            st = sts[l]
+            say(f"layer {l}: prefetch copied/missing {pf[l]}, step hits={st['hits']} m={st['misses']} q={st['q']}")
+            assert st["path"] == ecf.ECF_PATH_PREFILL and st["host"] == 0
+            assert (st["hits"], st["misses"], st["q"]) == (len(plan["hits"]), plan["m"], plan["q"])
+            ref, _ = _run(lay, lay.args(layer=l, router_logits=lgs[l], expert_ptrs=cs.resident_ptrs[l],
+                                        path=ecf.ECF_PATH_PREFILL), xs[l], T, d)
+            got = outs[l].cpu().numpy()
+            assert np.array_equal(got, ref), f"layer {l}: slot-pool prefill differs from the resident layer"
+            toks = np.arange(0, T, 5)
+            orc = oracle.moe_layer(xs[l].cpu(), _layer_experts(cs, cfg, l), k, lg=lgs[l].cpu(), w_dtype=w_dtype,
+                                   tokens=toks)
+            err = np.max(np.abs(got[toks] - orc["out"])) / np.sqrt(np.mean(orc["out"] ** 2))
+            say(f"layer {l}: err/RMS vs oracle {err:.2e} on {len(toks)} tokens")
+            assert err <= tol
+        if layers_of_slots < 2:
+            assert any(m > 0 for _, m in pf)  # part of a prefetch did not fit
+        for l in range(L):
+            for e in range(E):
+                want = ref_lru.resident(l, e)
+                assert ecf.ecf_cache_slot_of(cs.cache, l, e) == (-1 if want is None else want), (l, e)
+        stats = ecf.ecf_cache_get_stats(cs.cache)
+        assert {n: stats[n] for n in ref_lru.stats} == ref_lru.stats
+        # survivors warm decode
+        x = syn.activations(cfg, 4, layer=L - 1, batch=7, device="cuda")
+        lg = syn.router_logits(cfg, 4, layer=L - 1, step=7, device="cuda")
+        _, st = _run(lay, lay.args(layer=L - 1, router_logits=lg, cache=cs.cache), x, 4, d)
+        say(f"decode after prefill: unique={st['n_unique']} hits={st['hits']}")
+        assert st["hits"] > 0
+        if layers_of_slots >= 2:
+            assert st["hits"] == st["n_unique"]
+    finally:
+        cs.close()
 
 
 def test_bandwidth_profile_sane():

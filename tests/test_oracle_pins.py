@@ -347,3 +347,38 @@ def test_lru_resize_keeps_low_slots():
     c.resize(3)
     plan = c.step(1, {5: 1}, lambda m: m)
     assert plan["copied"] == {5: 2}
+
+
+def test_lru_prefetch_hand_trace():
+    # whole-layer prefetches held until their layer's step, a prefetch that does
+    # not fit (its missing expert reserved and filled by the step on demand), and
+    # the prefill path copying every miss: a hand-worked trace
+    tr = json.load(open(os.path.join(GOLD, "lru_prefetch_trace.json")))
+    c = oracle.LRURef(tr["n_slots"], tr["n_experts"])
+    for op in tr["ops"]:
+        if op["op"] == "prefetch":
+            assert c.prefetch(op["layer"]) == op["expect"]
+        else:
+            rows = {int(e): n for e, n in op["rows"].items()}
+            plan = c.step(op["layer"], rows, lambda m: m, prefill=op["prefill"])
+            assert sorted(plan["hits"]) == op["expect"]["hits"]
+            assert plan["copied"] == {int(e): s for e, s in op["expect"]["copied"].items()}
+    assert [[l, e, s] for (l, e), s in c.od.items()] == tr["final_lru_order"]
+    assert c.stats == tr["final_stats"]
+    assert c.held == {} and c.reserve == 0
+
+
+def test_lru_prefetch_never_starves_a_held_layer():
+    # capacity of one and a half layers: each prefetch places what the reserve
+    # allows, and every prefill step, in prefetch order, can copy what is missing
+    E = 8
+    c = oracle.LRURef(12, E)
+    c.prefetch(0)
+    for l in range(6):
+        nxt = c.prefetch(l + 1)
+        assert nxt["missing"] > 0
+        plan = c.step(l, {e: 1 for e in range(E)}, lambda m: m, prefill=True)
+        assert len(plan["hits"]) + len(plan["copied"]) == E
+    with pytest.raises(ValueError):  # one slot short of a whole layer
+        small = oracle.LRURef(E - 1, E)
+        small.step(0, {e: 1 for e in range(E)}, lambda m: m, prefill=True)
