@@ -449,6 +449,16 @@ def bench_prefill(torch, ecf, syn, name, steps, warmup, cpu=False, host_inputs=F
     if g1 and g2:
         res["gemm1_tflops"] = 2.0 * R * d * 2 * I / (g1 * 1e-6) / 1e12
         res["gemm2_tflops"] = 2.0 * R * I * d / (g2 * 1e-6) / 1e12
+    # hardware-counter figures of these GEMMs (FETCH_SIZE / WRITE_SIZE copy-calibrated,
+    # MFMA busy cycles), valid while the kernel sources match the recorded hash
+    cpath = os.path.join(ROOT, "profiles", "prefill_grouped_gemm_bf16_T4096_mxfp4_T8192_counters.md")
+    if os.path.exists(cpath):
+        cj = json.loads(open(cpath).read().split("```json", 1)[1].split("```", 1)[0])
+        if cj.get("source_hash") == src_hash("k_prefill.hip", "device_common.h"):
+            fmt = "mxfp4" if cfg.w_dtype == "mxfp4" else "bf16"
+            res["counters"] = {g: {kk: cj["gemms"][f"{fmt}_{g}"][kk] for kk in
+                                   ("traffic_ratio", "mfma_util", "clock_ghz", "flop_counted_over_algorithmic")}
+                               for g in ("gemm1", "gemm2")}
     if cpu and not host_inputs:  # the oracle beside it, on batch 0 (what `counts` holds)
         lay.forward(lay.args(router_logits=lgs[0], expert_ptrs=pool.ptrs), xs[0], out, False)
         torch.cuda.synchronize()
