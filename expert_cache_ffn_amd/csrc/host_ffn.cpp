@@ -353,6 +353,20 @@ void dots_any(Isa isa, int wf, RowRef row, const float *const *xs, const uint16_
 
 }  // namespace
 
+// Per-thread scratch of the expert tasks, reused across tasks and calls.  Each
+// thread that runs a task enters this function, so its copy is constructed
+// there on first use and destroyed when the thread ends.
+struct Scratch {
+    std::vector<const float *> xs;
+    std::vector<const uint16_t *> xb;
+    std::vector<float> a, b;
+};
+static Scratch &scratch()
+{
+    static thread_local Scratch s;
+    return s;
+}
+
 int host_experts(HostPool &pool, const ecf_shape &s, const BlobLayout &lay,
                  const std::vector<HostExpertJob> &jobs, const void *x, int T, float *y)
 {
@@ -380,18 +394,10 @@ int host_experts(HostPool &pool, const ecf_shape &s, const BlobLayout &lay,
     constexpr int CH = 16, CHD = 64;
     const int gu_chunks = (I + CH - 1) / CH, dn_chunks = (d + CHD - 1) / CHD;
     const int nj = (int)jobs.size();
-    // per-thread scratch, reused across tasks and calls (the pool's threads persist)
-    struct Scratch {
-        std::vector<const float *> xs;
-        std::vector<const uint16_t *> xb;
-        std::vector<float> a, b;
-    };
-    static thread_local Scratch tls;
-
     pool.parallel_for(nj * gu_chunks, [&](int task) {
         const HostExpertJob &jb = jobs[task / gu_chunks];
         const int nr = (int)jb.rows.size();
-        Scratch &sc = tls;
+        Scratch &sc = scratch();
         sc.xs.resize(nr);
         sc.xb.resize(nr);
         sc.a.resize(nr);
@@ -419,7 +425,7 @@ int host_experts(HostPool &pool, const ecf_shape &s, const BlobLayout &lay,
         const HostExpertJob &jb = jobs[task / dn_chunks];
         const int nr = (int)jb.rows.size();
         const float *hj = h.data() + hoff[task / dn_chunks];
-        Scratch &sc = tls;
+        Scratch &sc = scratch();
         sc.xs.resize(nr);
         sc.a.resize(nr);
         std::vector<const float *> &hs = sc.xs;
