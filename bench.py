@@ -615,14 +615,27 @@ def cached_setup(torch, ecf, syn, T=16, steps=16, warmup=16, n_blobs=256, w_dtyp
     hb = host.data_ptr()
     blob_of = lambda l, e: (l * 97 + e) % n_blobs
     pool = [hb + blob_of(l, e) * S for l in range(L) for e in range(E)]
-    n_logits = warmup + steps   # fresh routing every step: no replayed trace inflates the hit rate
-    lgs = [[syn.router_logits(cfg, T, layer=l, step=s, device="cuda") for l in range(L)] for s in range(n_logits)]
+    ctx = dict(cfg=cfg, shape=shape, S=S, L=L, E=E, d=d, n_slots=n_slots, host=host, slots=slots, w_dtype=w_dtype,
+               pool=pool, blob_of=blob_of, n_blobs=n_blobs, steps=steps, warmup=warmup,
+               cstream=torch.cuda.Stream())
+    cached_tokens(torch, syn, ctx, T)
+    return ctx
+
+
+def cached_tokens(torch, syn, ctx, T):
+    """Set the batch size of the cached-decode workload: per-step router logits
+    (fresh every step, so no replayed trace inflates the hit rate), the layer's
+    workspace, activations, the fp32 residual and the bf16 next-layer input."""
+    from expert_cache_ffn_amd.layer import Layer
+    cfg, L, d = ctx["cfg"], ctx["L"], ctx["d"]
+    ctx.pop("lgs", None)
+    n_logits = ctx["warmup"] + ctx["steps"]
+    ctx.update(T=T, lgs=[[syn.router_logits(cfg, T, layer=l, step=s, device="cuda") for l in range(L)]
+                         for s in range(n_logits)],
+               layer=Layer(ctx["shape"], T), xa=syn.activations(cfg, T, device="cuda"),
+               res_f=torch.empty((T, d), dtype=torch.float32, device="cuda"),
+               act=torch.empty((T, d), dtype=torch.bfloat16, device="cuda"))
     torch.cuda.synchronize()  # setup queued on the default stream lands before the copy stream fills slots
-    return dict(cfg=cfg, shape=shape, S=S, L=L, E=E, T=T, d=d, n_slots=n_slots, host=host, slots=slots, w_dtype=w_dtype,
-                pool=pool, blob_of=blob_of, lgs=lgs, n_blobs=n_blobs, steps=steps, warmup=warmup,
-                layer=Layer(shape, T), cstream=torch.cuda.Stream(), xa=syn.activations(cfg, T, device="cuda"),
-                res_f=torch.empty((T, d), dtype=torch.float32, device="cuda"),
-                act=torch.empty((T, d), dtype=torch.bfloat16, device="cuda"))
 
 
 def static_hot_set(syn, cfg, n_slots):
@@ -762,6 +775,7 @@ def main():
     ap.add_argument("--cached-steps", type=int, default=12)
     ap.add_argument("--cached-warmup", type=int, default=None, help="cached decode warm-up steps (default: --cached-steps)")
     ap.add_argument("--policies", default=",".join(POLICIES), help="policies the 'policies' workload compares")
+    ap.add_argument("--cached-tokens", default="1,4,16", help="cached-decode batch sizes (cached, policies)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run one plain 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--host-inputs", action="store_true",
@@ -831,15 +845,17 @@ def main():
         bw = None
         if wl & {"bandwidth", "policies"}:
             bw = also["bandwidth_profile"] = bench_bandwidth(torch, ecf, ctx)
-        if "cached" in wl:
-            also["cached_decode_43L_T16"] = bench_cached(torch, ecf, syn, ctx, "lru_qstar")
-        if "policies" in wl:
-            pol = {p: (dict(also["cached_decode_43L_T16"]) if p == "lru_qstar" and "cached" in wl
-                       else bench_cached(torch, ecf, syn, ctx, p, bw))
-                   for p in POLICIES if p in args.policies.split(",")}
-            for r in pol.values():
-                r.pop("q_hist")
-            also["cached_policies_43L_T16"] = pol
+        for T in (int(t) for t in args.cached_tokens.split(",")):
+            cached_tokens(torch, syn, ctx, T)
+            if "cached" in wl:
+                also[f"cached_decode_43L_T{T}"] = bench_cached(torch, ecf, syn, ctx, "lru_qstar")
+            if "policies" in wl:
+                pol = {p: (dict(also[f"cached_decode_43L_T{T}"]) if p == "lru_qstar" and "cached" in wl
+                           else bench_cached(torch, ecf, syn, ctx, p, bw))
+                       for p in POLICIES if p in args.policies.split(",")}
+                for r in pol.values():
+                    r.pop("q_hist")
+                also[f"cached_policies_43L_T{T}"] = pol
         del ctx
         torch.cuda.empty_cache()
     if "cached_fp4" in wl:

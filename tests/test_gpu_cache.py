@@ -380,6 +380,73 @@ def test_streamed_prefill_through_slot_pool(w_dtype, layers_of_slots):
         cs.close()
 
 
+def _hot_set(cfg, n_slots):
+    """The n_slots most popular (layer, expert) pairs of the Zipf recipe."""
+    per, extra = divmod(n_slots, cfg.layers)
+    return [sorted(int(e) for e in (syn.popularity_rank(cfg, l) <= per + (1 if l < extra else 0)).nonzero().flatten())
+            for l in range(cfg.layers)]
+
+
+@pytest.mark.parametrize("policy", ["static_hot", "all_pcie"])
+def test_policy_ablation_small(policy):
+    """The two comparison policies at equal capacity (37% of the pairs), through
+    the C ABI: a static hot subset (the most popular pairs bound once with
+    expert_cache_lookup / expert_cache_evict and filled, then every miss on the
+    host, q = 0) and the shared LRU with every miss copied (q = m).  Each step's
+    output matches the oracle and the all-resident layer, and its hit / miss /
+    copy counts match a Python reference of the policy (a fixed set for the
+    static subset, the reference LRU for all-PCIe)."""
+    E, L, T, k = 16, 3, 4, 4
+    cfg = syn.gen.Config(106, "pol", (T,), 512, E, 256, k, "bf16", "bf16", "zipf", layers=L)
+    d = cfg.hidden
+    n_slots = int(0.37 * L * E)
+    cs = CachedSetup(cfg, L, n_slots=n_slots)
+    lay = Layer(cs.shape, T)
+    cstream = torch.cuda.Stream()
+    try:
+        if policy == "static_hot":
+            hot = _hot_set(cfg, n_slots)
+            assert sum(len(h) for h in hot) == n_slots
+            for l, h in enumerate(hot):
+                assert ecf.expert_cache_lookup(cs.cache, l, h) == [-1] * len(h)
+                slots, victims = ecf.expert_cache_evict(cs.cache, l, h)
+                assert victims == [-1] * len(h)
+                for e, sl in zip(h, slots):
+                    cs.slots[sl].copy_(cs.dev_blobs[cs.blob_of(l, e)])
+            torch.cuda.synchronize()
+            q_mode = ecf.ECF_Q_ALL_HOST
+        else:
+            ref_lru = oracle.LRURef(n_slots, E)
+            q_mode = ecf.ECF_Q_ALL_GPU
+        for step in range(12):
+            l = step % L
+            x = syn.activations(cfg, T, layer=l, batch=step, device="cuda")
+            lg = syn.router_logits(cfg, T, layer=l, step=step, device="cuda")
+            got, st = _run(lay, lay.args(layer=l, router_logits=lg, cache=cs.cache, q_mode=q_mode,
+                                         copy_stream=cstream), x, T, d)
+            ref, _ = _run(lay, lay.args(layer=l, router_logits=lg, expert_ptrs=cs.resident_ptrs[l]), x, T, d)
+            orc = oracle.moe_layer(x.cpu(), _layer_experts(cs, cfg, l), k, lg=lg.cpu())
+            rows = _rows_of(lg, k)
+            if policy == "static_hot":
+                hits = len(set(rows) & set(hot[l]))
+                want = (hits, len(rows) - hits, 0, len(rows) - hits)
+            else:
+                plan = ref_lru.step(l, rows, lambda m: m)
+                want = (len(plan["hits"]), plan["m"], plan["q"], len(plan["host"]))
+            assert (st["hits"], st["misses"], st["q"], st["host"]) == want, (step, st, want)
+            e_res = np.max(np.abs(got - ref)) / np.sqrt(np.mean(ref ** 2))
+            e_orc = np.max(np.abs(got - orc["out"])) / np.sqrt(np.mean(orc["out"] ** 2))
+            say(f"{policy} step {step}: hits={st['hits']} m={st['misses']} q={st['q']} host={st['host']} "
+                f"err/RMS vs resident {e_res:.2e}, vs oracle {e_orc:.2e}")
+            assert e_res <= SPLIT_TOL and e_orc <= 2e-2
+        if policy == "static_hot":  # the subset never changed
+            for l, h in enumerate(hot):
+                assert all(ecf.ecf_cache_slot_of(cs.cache, l, e) >= 0 for e in h)
+            assert ecf.ecf_cache_get_stats(cs.cache)["evictions"] == 0
+    finally:
+        cs.close()
+
+
 def test_bandwidth_profile_sane():
     """ecf_bandwidth_profile on a few small pinned blobs: every rate positive,
     b_h the sum of the concurrent rates, and its ratio usable by qstar_split."""
