@@ -741,6 +741,9 @@ int forward_impl(const ecf_layer_args *a, const void *d_x, int32_t T, float *d_o
                 return rc;
             lg = dl;
         }
+        // One token on the decode path, all experts resident, MXFP4 weights: the
+        // down projection and the combine run as one kernel.
+        const bool fused_down = !a->cache && path == ECF_PATH_DECODE && down_combine1_ok(s, T);
         if ((rc = launch_route(s, lg, T, ro, stream)) != ECF_OK)
             return rc;
 
@@ -751,10 +754,16 @@ int forward_impl(const ecf_layer_args *a, const void *d_x, int32_t T, float *d_o
             if ((rc = cache_step(a, d_x, T, ro, wl, ws, lay, path, stats, &tab, &host_part)) != ECF_OK)
                 return rc;
             ex.ptrs = tab;
+        } else if (fused_down) {
+            float *H = (float *)(ws + wl.hbuf);
+            if ((rc = launch_decode_gateup(s, ex, ro, d_x, T, H, stream)) != ECF_OK ||
+                (rc = launch_decode_down_combine1(s, ex, ro, H, a->d_residual, d_out, a->d_out_act, stream)) != ECF_OK)
+                return rc;
         } else if ((rc = launch_experts(s, ex, ro, d_x, T, wl, ws, path, stream)) != ECF_OK) {
             return rc;
         }
-        if ((rc = launch_combine(s, ex, ro, (const float *)(ws + wl.ybuf), T, a->d_residual, host_part, d_out,
+        if (!fused_down &&
+            (rc = launch_combine(s, ex, ro, (const float *)(ws + wl.ybuf), T, a->d_residual, host_part, d_out,
                                  a->d_out_act, stream)) != ECF_OK)
             return rc;
         const int R = T * s.top_k;

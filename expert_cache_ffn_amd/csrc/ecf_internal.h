@@ -100,12 +100,18 @@ struct ExpertTables {
 
 int launch_decode_gateup(const ecf_shape &s, const ExpertTables &ex, const RouteOut &o, const void *x,
                          int T, float *H, hipStream_t st);
+
 int launch_decode_down(const ecf_shape &s, const ExpertTables &ex, const RouteOut &o, const float *H,
                        int T, float *Y, hipStream_t st);
 int launch_prefill_gemm1(const ecf_shape &s, const ExpertTables &ex, const RouteOut &o, const void *x,
                          int T, uint16_t *H, hipStream_t st);
 int launch_prefill_gemm2(const ecf_shape &s, const ExpertTables &ex, const RouteOut &o, const uint16_t *H,
                          int T, float *Y, hipStream_t st);
+// One token (T = 1, k <= 8, MXFP4 weights with bf16 activations): the down
+// projection and the combine in one kernel, no Y in memory.
+bool down_combine1_ok(const ecf_shape &s, int T);
+int launch_decode_down_combine1(const ecf_shape &s, const ExpertTables &ex, const RouteOut &o, const float *H,
+                                const float *residual, float *out, void *out_act, hipStream_t st);
 int launch_combine(const ecf_shape &s, const ExpertTables &ex, const RouteOut &o, const float *Y, int T,
                    const float *residual, const float *host_part, float *out, void *out_act,
                    hipStream_t st);

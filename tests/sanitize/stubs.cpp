@@ -9,6 +9,9 @@ int launch_router_logits(const ecf_shape &, const void *, const void *, int, flo
 int launch_route(const ecf_shape &, const float *, int, const RouteOut &, hipStream_t) { std::abort(); }
 int launch_decode_gateup(const ecf_shape &, const ExpertTables &, const RouteOut &, const void *, int, float *,
                          hipStream_t) { std::abort(); }
+bool down_combine1_ok(const ecf_shape &, int) { return false; }
+int launch_decode_down_combine1(const ecf_shape &, const ExpertTables &, const RouteOut &, const float *, const float *,
+                                float *, void *, hipStream_t) { std::abort(); }
 int launch_decode_down(const ecf_shape &, const ExpertTables &, const RouteOut &, const float *, int, float *,
                        hipStream_t) { std::abort(); }
 int launch_prefill_gemm1(const ecf_shape &, const ExpertTables &, const RouteOut &, const void *, int, uint16_t *,

@@ -164,6 +164,53 @@ def test_one_token(w, E, k, I):
     assert np.array_equal(res["out"], base["out"] + r.cpu().numpy())
 
 
+# ---- one token with MXFP4 experts: down projection and combine in one kernel -------------
+
+@pytest.mark.parametrize("w,T,E,k,I", [("mxfp4", 1, 32, 8, 256), ("mxfp4", 1, 16, 6, 512), ("mxfp4", 1, 8, 1, 128),
+                                       ("mxfp4", 1, 8, 2, 192), ("mxfp4", 2, 16, 4, 256), ("bf16", 1, 16, 6, 512)])
+def test_one_token_fused_down_combine(w, T, E, k, I):
+    """One token, MXFP4 weights, I % 128 == 0: the down projection and the combine
+    run as one kernel (the other cases take the separate kernels).  Routing,
+    outputs, the residual add against the oracle."""
+    cfg = cfg_small(experts=E, top_k=k, inter=I, w_dtype=w, cid=150 + T + k)
+    say(f"case: one token fused down+combine {w} T={T} E={E} k={k} I={I}")
+    c = Case(cfg, T)
+    base = c.run()
+    assert base["stats"]["path"] == ecf.ECF_PATH_DECODE
+    compare(base, c.oracle(), 1e-4, f"fused down {w} T={T} E={E} k={k}")
+    r = torch.randn(T, cfg.hidden, dtype=torch.float32, device="cuda")
+    res = c.run(residual=r)
+    assert np.array_equal(res["out"], base["out"] + r.cpu().numpy())
+
+
+def test_one_token_mxfp4_graph_replay():
+    """One MXFP4 token through a captured graph (fused down + combine): every
+    replay equals the eager call, with eager work between."""
+    from expert_cache_ffn_amd.layer import Layer
+    cfg = cfg_small(experts=16, top_k=6, w_dtype="mxfp4", cid=160)
+    c = Case(cfg, 1)
+    eager = c.run()["out"]
+    lay = Layer(c.shape, 1)
+    s = torch.cuda.Stream()
+    x = c.x.cuda().contiguous()
+    wr = c.router_w.cuda().contiguous()
+    out = torch.zeros((1, cfg.hidden), dtype=torch.float32, device="cuda")
+    with torch.cuda.stream(s):
+        a = lay.args(router_w=wr, expert_ptrs=c.pool.ptrs, stream=s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            rc = ecf.lib().moe_layer_forward(a, x.data_ptr(), 1, out.data_ptr(), None)
+        assert rc == 0
+    for rep in range(4):
+        out.fill_(float("nan"))
+        junk = torch.randn(1000, 1000, device="cuda") @ torch.randn(1000, 1000, device="cuda")
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), eager), f"replay {rep} differs"
+        del junk
+
+
 # ---- prefill bf16 (grouped MFMA GEMM) ---------------------------------------------------
 
 # T*k above 2048 takes the multi-block counting sort: 1500 x 2 over 4 experts and
