@@ -380,6 +380,70 @@ def test_streamed_prefill_through_slot_pool(w_dtype, layers_of_slots):
         cs.close()
 
 
+def test_prefetch_holds_against_decode_and_resize():
+    """A pending whole-layer prefetch next to decode steps of other layers: its
+    entries are held (a decode step copying every miss never evicts them, and
+    fewer slots are then available to it), a second prefetch of the layer adds
+    nothing, the layer's own step ends the hold, and a resize waits for pending
+    copies and drops the holds.  Every step's output matches the all-resident
+    layer within 1e-5, and the cache state follows the reference LRU."""
+    E, L, T, k = 8, 3, 4, 2
+    cfg = syn.gen.Config(107, "ph", (T,), 512, E, 256, k, "bf16", "bf16", "zipf", layers=L)
+    d = cfg.hidden
+    n_slots = 12
+    cs = CachedSetup(cfg, L, n_slots=n_slots)
+    lay = Layer(cs.shape, T)
+    cstream = torch.cuda.Stream()
+    ref = oracle.LRURef(n_slots, E)
+    blob = ecf.ecf_expert_bytes(cs.shape)
+
+    def step(l, s, q_mode=ecf.ECF_Q_ALL_GPU):
+        x = syn.activations(cfg, T, layer=l, batch=s, device="cuda")
+        lg = syn.router_logits(cfg, T, layer=l, step=s, device="cuda")
+        got, st = _run(lay, lay.args(layer=l, router_logits=lg, cache=cs.cache, q_mode=q_mode, copy_stream=cstream),
+                       x, T, d)
+        want, _ = _run(lay, lay.args(layer=l, router_logits=lg, expert_ptrs=cs.resident_ptrs[l]), x, T, d)
+        err = np.max(np.abs(got - want)) / np.sqrt(np.mean(want ** 2))
+        plan = ref.step(l, _rows_of(lg, k), (lambda m: m) if q_mode == ecf.ECF_Q_ALL_GPU else (lambda m: 0))
+        assert (st["hits"], st["misses"], st["q"]) == (len(plan["hits"]), plan["m"], plan["q"]), (l, s, st, plan)
+        assert err <= SPLIT_TOL
+        return st
+
+    def state_matches():
+        for l in range(L):
+            for e in range(E):
+                want = ref.resident(l, e)
+                assert ecf.ecf_cache_slot_of(cs.cache, l, e) == (-1 if want is None else want), (l, e)
+
+    try:
+        step(0, 0)
+        step(2, 1)
+        assert ecf.prefetch_layer(cs.cache, 1, blob, cstream.cuda_stream) == (lambda r: (len(r["copied"]), r["missing"]))(
+            ref.prefetch(1))
+        assert ecf.prefetch_layer(cs.cache, 1, blob, cstream.cuda_stream) == (0, ref.prefetch(1)["missing"])
+        state_matches()
+        for s_ in range(2, 6):  # decode steps of layers 0 and 2 while layer 1 is held
+            step(0 if s_ % 2 == 0 else 2, s_)
+            state_matches()
+        assert all(ecf.ecf_cache_slot_of(cs.cache, 1, e) >= 0 for e in range(E) if ref.resident(1, e) is not None)
+        st = step(1, 6)  # the held layer's own step: its prefetched experts are hits
+        assert st["hits"] > 0
+        state_matches()
+        # a prefetch left pending across a resize: the copies land, the hold ends
+        ecf.prefetch_layer(cs.cache, 2, blob, cstream.cuda_stream)
+        ref.prefetch(2)
+        ecf.ecf_cache_resize(cs.cache, 6)
+        ref.resize(6)
+        state_matches()
+        step(2, 7)
+        step(0, 8)
+        state_matches()
+        stats = ecf.ecf_cache_get_stats(cs.cache)
+        assert {n: stats[n] for n in ref.stats} == ref.stats
+    finally:
+        cs.close()
+
+
 def _hot_set(cfg, n_slots):
     """The n_slots most popular (layer, expert) pairs of the Zipf recipe."""
     per, extra = divmod(n_slots, cfg.layers)
