@@ -661,8 +661,52 @@ POLICIES = {
 }
 
 
-def bench_cached(torch, ecf, syn, ctx, policy="lru_qstar", bw=None):
-    """One policy on the shared cached-decode setup; returns throughput and traffic."""
+def cached_oracle_check(torch, syn, ctx, rec, lgs_step):
+    """The oracle layer by layer on one recorded cached-decode step: each layer's
+    GPU input (the previous layer's bf16 output) and residual in, through the
+    oracle's MoE layer on that layer's (aliased) host blobs; the GPU's layer
+    output must equal residual + MoE within 2e-2 of the MoE part's RMS.  Timed:
+    the oracle's tokens/s over the 43 layers (a bounded sample of the cached
+    workload: one step)."""
+    import numpy as np
+    import oracle
+    from expert_cache_ffn_amd.layer import blob_sections
+    cfg, L, E, d, I, k = ctx["cfg"], ctx["L"], ctx["E"], ctx["d"], ctx["cfg"].inter, ctx["cfg"].top_k
+    secs = dict(blob_sections(ctx["shape"]))
+    host = ctx["host"]
+    cache = {}
+
+    def expert(b):
+        if b not in cache:
+            blob = host[b]
+            n = d * I * 2
+            cache[b] = {nm: blob[off:off + n].view(torch.bfloat16).view(I if nm != "w_down" else d,
+                                                                        d if nm != "w_down" else I)
+                        for nm, off in secs.items()}
+        return cache[b]
+
+    worst, el, T = 0.0, 0.0, rec[0][0].shape[0]
+    for l, (x_in, r_in, out) in enumerate(rec):
+        experts = [expert(ctx["blob_of"](l, e)) for e in range(E)]
+        t0 = time.perf_counter()
+        moe = oracle.moe_layer(x_in, experts, k, lg=lgs_step[l].cpu())["out"]
+        el += time.perf_counter() - t0
+        err = float(np.max(np.abs(out - (r_in + moe)))) / float(np.sqrt(np.mean(moe ** 2)))
+        worst = max(worst, err)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    r = {"value": T / el, "unit": "tokens/s (43-layer step)", "cores": threads, "kind": "oracle",
+         "sample": f"one step of {T} tokens through all {L} layers ({el:.1f} s of CPU time)",
+         "checked_against_gpu": {"layers": L, "max_err_over_moe_rms": worst, "tolerance": 2e-2,
+                                 "ok": bool(worst <= 2e-2)}}
+    log(f"cached oracle: {r['value']:.2f} tok/s over {L} layers on {threads} threads; GPU layers within "
+        f"{worst:.2e} of the oracle's (x RMS of each layer's MoE output)")
+    return r
+
+
+def bench_cached(torch, ecf, syn, ctx, policy="lru_qstar", bw=None, oracle_check=False):
+    """One policy on the shared cached-decode setup; returns throughput and traffic.
+    oracle_check: afterwards one more step is recorded layer by layer and checked
+    against (and timed beside) the oracle."""
     L, E, T, S = ctx["L"], ctx["E"], ctx["T"], ctx["S"]
     steps, warmup, lgs, lay = ctx["steps"], ctx["warmup"], ctx["lgs"], ctx["layer"]
     n_logits = len(lgs)
@@ -687,13 +731,19 @@ def bench_cached(torch, ecf, syn, ctx, policy="lru_qstar", bw=None):
     qhist = {}
     res_f, act, xa = ctx["res_f"], ctx["act"], ctx["xa"]
 
-    def one_step(s, record):
+    def one_step(s, record, layers_out=None):
         x = xa
         res_f.zero_()
         for l in range(L):
             a = lay.args(layer=l, router_logits=lgs[s % n_logits][l], cache=cache, b_p=b_p, b_h=b_h,
                          q_mode=q_mode, copy_stream=ctx["cstream"], residual=res_f, out_act=act)
+            if layers_out is not None:
+                torch.cuda.synchronize()
+                x_in, r_in = x.cpu().clone(), res_f.cpu().numpy().copy()
             st = lay.forward(a, x, res_f)
+            if layers_out is not None:
+                torch.cuda.synchronize()
+                layers_out.append((x_in, r_in, res_f.cpu().numpy().copy()))
             x = act
             if record:
                 totals["unique"] += st["n_unique"]
@@ -720,6 +770,11 @@ def bench_cached(torch, ecf, syn, ctx, policy="lru_qstar", bw=None):
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     st2 = ecf.ecf_cache_get_stats(cache)
+    oracle_res = None
+    if oracle_check:
+        rec = []
+        one_step(warmup + steps, False, rec)
+        oracle_res = cached_oracle_check(torch, syn, ctx, rec, lgs[(warmup + steps) % n_logits])
     ecf.ecf_cache_destroy(cache)
     miss_cold = (st1["misses"] - st0["misses"]) / max(1, st1["lookups"] - st0["lookups"])
     miss_steady = (st2["misses"] - st1["misses"]) / max(1, st2["lookups"] - st1["lookups"])
@@ -734,6 +789,8 @@ def bench_cached(torch, ecf, syn, ctx, policy="lru_qstar", bw=None):
                ms_wait_route_per_step=totals["wait"] / steps, ms_host_ffn_per_step=totals["hostms"] / steps,
                q_hist={str(q): n for q, n in sorted(qhist.items())}, host_blobs=ctx["n_blobs"],
                host_threads="default (min(16, hardware threads))")
+    if oracle_res is not None:
+        res["cpu_oracle"] = oracle_res
     log(f"cached {ctx['w_dtype']} [{policy}]: {res['ms_per_step']:.1f} ms/step ({L} layers), {res['tokens_per_s']:.1f} tok/s, "
         f"steady miss rate {100 * miss_steady:.1f}%, PCIe {res['pcie_GBps']:.1f} GB/s, "
         f"host {res['host_read_GBps']:.1f} GB/s, HBM (expert weights) {res['hbm_expert_GBps']:.1f} GB/s")
@@ -848,7 +905,8 @@ def main():
         for T in (int(t) for t in args.cached_tokens.split(",")):
             cached_tokens(torch, syn, ctx, T)
             if "cached" in wl:
-                also[f"cached_decode_43L_T{T}"] = bench_cached(torch, ecf, syn, ctx, "lru_qstar")
+                also[f"cached_decode_43L_T{T}"] = bench_cached(
+                    torch, ecf, syn, ctx, "lru_qstar", oracle_check=T == 16 and not args.no_cpu_baseline)
             if "policies" in wl:
                 pol = {p: (dict(also[f"cached_decode_43L_T{T}"]) if p == "lru_qstar" and "cached" in wl
                            else bench_cached(torch, ecf, syn, ctx, p, bw))
