@@ -79,3 +79,37 @@ def test_noalloc_refuses_oversize_and_cache_mode():
         ecf.moe_layer_forward_noalloc(a, 256, 4, 256)
     assert ei.value.code == ecf.ECF_EUNSUPPORTED
     say(f"noalloc: {T_big} decode-shape tokens exceed the {cap}-byte scratch; cache mode refused")
+
+
+def test_noalloc_one_token_mxfp4_and_graph_capture():
+    """The allocation-free call on one MXFP4 token (the fused down + combine
+    kernel) equals moe_layer_forward bit for bit, and captured in a HIP graph it
+    gives the eager result on every replay, with eager work in between."""
+    cfg = syn.gen.Config(176, "noalloc", (1,), 1024, 16, 256, 6, "mxfp4", "bf16", "router")
+    say("case: noalloc, one MXFP4 token, eager and graph replays")
+    case = Case(cfg, 1)
+    lay = Layer(case.shape, 1)
+    ref, _ = _call(ecf.moe_layer_forward, case, lay, 1, ecf.ECF_PATH_AUTO)
+    got, st = _call(ecf.moe_layer_forward_noalloc, case, lay, 1, ecf.ECF_PATH_AUTO)
+    assert st["path"] == ecf.ECF_PATH_DECODE
+    for key in ("idx", "gate", "counts", "perm", "out"):
+        assert np.array_equal(got[key], ref[key]), key
+    s = torch.cuda.Stream()
+    x = case.x.to("cuda").contiguous()
+    wr = case.router_w.to("cuda").contiguous()
+    out = torch.zeros((1, cfg.hidden), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        a = lay.args(router_w=wr, expert_ptrs=case.pool.ptrs, stream=s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            rc = ecf.lib().moe_layer_forward_noalloc(a, x.data_ptr(), 1, out.data_ptr(), None)
+        assert rc == 0
+    for rep in range(4):
+        out.fill_(float("nan"))
+        junk = torch.randn(1000, 1000, device="cuda") @ torch.randn(1000, 1000, device="cuda")
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), ref["out"]), f"replay {rep} differs"
+        del junk
