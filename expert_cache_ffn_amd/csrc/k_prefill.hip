@@ -15,15 +15,18 @@
 //
 // Block = NW waves as WM x (NW / WM), tile BM rows x BNT weight rows, BK = 64
 // (bf16: 8 waves on 128 x 256, each 64 x 64; MXFP4: 8 waves on 320 x 256, each
-// 160 rows x 64 weight rows, i.e. up to 5 x 2 MFMA 32x32 fragments).  Software pipeline of depth 2 through
-// registers: in program order the loads of k-tile kt+2 come before the MFMAs
-// of k-tile kt and the LDS stores of k-tile kt+1 after them (the compiler's
-// schedule of that order measured faster than pinning it with scheduling
-// barriers).  Operands arrive by raw buffer loads: one 32-bit offset register
-// per row, the k-tile's column in a scalar offset.  (Direct global->LDS loads
-// were measured against: the compiler cannot tell which in-flight LDS DMA a
-// later LDS read depends on and drains them all, which serialises the
-// pipeline.)
+// 160 rows x 64 weight rows, i.e. up to 5 x 2 MFMA 32x32 fragments).
+//
+// Operand tiles go from global memory straight into LDS (buffer_load ... lds,
+// 16 bytes per lane, gfx950), three stages deep: while the MFMAs of k-tile kt
+// run, the loads of k-tile kt+2 are in flight and those of kt+1 land.  Each
+// stage is its own LDS array, so the compiler's wait before an LDS read covers
+// only the loads into that stage; the end of a k-tile waits for this wave's
+// loads of k-tile kt+1 and then meets the other waves (stage_barrier).  No
+// operand passes through registers on its way to LDS.  Against a depth-2
+// pipeline through registers on one GPU: MXFP4 GEMM1 2145 -> 2038 us, GEMM2
+// 1129 -> 1077 us, bf16 GEMM1 752 -> 745 us.  Loads use raw buffer resources:
+// one 32-bit offset register per row, the k-tile's column in a scalar offset.
 //
 // bf16 rows of 64 elements (eight 16-B chunks) sit in LDS XOR-swizzled (see
 // swz), so the 32 rows one MFMA operand read touches spread over the banks.
@@ -47,7 +50,10 @@ constexpr int BK = 64;  // reduction elements per stage
 // of r.  A 16-B-per-lane read of one chunk over rows r0..r0+15 then touches 16
 // distinct 16-B bank groups mod 256 B (and any 8 aligned rows 8 distinct groups
 // mod 128 B), so it is conflict-free whether the LDS serves 8 or 16 lanes of a
-// 128-bit access per cycle.
+// 128-bit access per cycle.  (A layout with 8-row blocks stored chunk-major,
+// which needs one LDS address register per stage instead of one per chunk,
+// measured slower: its global->LDS loads put consecutive lanes on different
+// rows, so the loads coalesce worse; bf16 GEMM1 743 -> 837 us.)
 __device__ __forceinline__ int swz(int row, int ch) { return row * 8 + (ch ^ (row & 7) ^ ((row >> 3) & 1)); }
 
 // MXFP4 LDS tile: row = 32 bytes (two 16-B halves); the halves swap with bit 2
@@ -81,23 +87,11 @@ __device__ __forceinline__ bf16x8_t cvt_mx8(uint32_t w, float s)
     return r;
 }
 
-// One stage of global data held in registers between load and LDS store.
-// BNT = weight rows per block tile; NBL = 16-B B chunks per thread and stage.
-// A stage covers KS sub-tiles of BK = 64 reduction elements each.
-template <bool MX, int BM, int BNT, int KS, int NTH>
-struct Stage {
-    static constexpr int NAL = BM * 8 / NTH;                // 16-B A chunks per thread and sub-tile
-    static constexpr int NBL = (MX ? BNT * 2 : BNT * 8) / NTH;  // 16-B B chunks per thread and sub-tile
-    static_assert(NAL >= 1 && NBL >= 1, "tile too small for the block");
-    u32x4_t a[NAL * KS];      // A: rows (tid>>3) + (NTH/8)q, chunk tid&7, per sub-tile
-    u32x4_t b[NBL * KS];      // B bf16: rows (tid>>3) + (NTH/8)q; MX: rows (tid>>1) + (NTH/2)q, half tid&1
-    uint32_t s;               // MX: the 2*KS scale bytes of row tid (tid < BNT)
-};
-
 // Operand loads are raw buffer loads: a block-uniform resource (base and byte
 // size, in scalar registers), this thread's 32-bit row offset, and the k-tile's
 // column offset as the uniform soffset -- one VGPR per row and no per-k-tile
-// address arithmetic in vector registers.  A load at or past the size returns 0.
+// address arithmetic in vector registers.  A lane whose offset lies at or past
+// the size reads zeros and touches no memory.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
@@ -105,71 +99,45 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
 }
 
-template <bool MX, int BM, int BNT, int NTH>
-struct Ptrs {
-    uint32_t a[Stage<MX, BM, BNT, 1, NTH>::NAL];  // A rows, this thread's 16-B chunk (bytes from A's base)
-    uint32_t b[Stage<MX, BM, BNT, 1, NTH>::NBL];  // B rows within the blob, this thread's 16-B chunk
-    uint32_t s;                                   // MX: this thread's scale row within the blob
-};
-
-// BAUX: cache policy of the weight loads (2 = non-temporal, 0 = default).
-template <int BAUX, bool MX, int BM, int BNT, int KS, int NTH>
-__device__ __forceinline__ void gload(Stage<MX, BM, BNT, KS, NTH> &st, const Ptrs<MX, BM, BNT, NTH> &p, rsrc_t ra,
-                                      rsrc_t rb, int kt, int tid)
+// 16 bytes per lane from a raw buffer straight into LDS: lane l's bytes land at
+// lds + 16 l (the LDS base is wave-uniform; it goes to M0).  AUX is the cache
+// policy.  The 16-byte form is gfx950's; hipcc's host pass cannot check it
+// against a gfx950 target, so the body exists in the device pass only (the
+// host pass needs no more than the kernel's signature).
+template <int AUX>
+__device__ __forceinline__ void lds_load16(rsrc_t r, u32x4_t *lds, uint32_t voff, uint32_t soff)
 {
-    constexpr int NAL = Stage<MX, BM, BNT, KS, NTH>::NAL, NBL = Stage<MX, BM, BNT, KS, NTH>::NBL;
-#pragma unroll
-    for (int sub = 0; sub < KS; ++sub) {
-        const int col = (kt * KS + sub) * BK;  // first reduction element of the sub-tile
-#pragma unroll
-        for (int q = 0; q < NAL; ++q)
-            st.a[sub * NAL + q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, p.a[q], col * 2, 0));
-#pragma unroll
-        for (int q = 0; q < NBL; ++q)
-            st.b[sub * NBL + q] = __builtin_bit_cast(
-                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rb, p.b[q], MX ? col / 2 : col * 2, BAUX));
-    }
-    // every thread loads (threads past BNT re-read row 0's scales), so the number
-    // of loads in flight is the same on every path and the compiler's load
-    // counters can wait for exactly the older stage
-    if (MX)
-        st.s = KS == 2 ? __builtin_amdgcn_raw_buffer_load_b32(rb, p.s, kt * 4, 0)
-                       : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, p.s, kt * 2, 0);
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, AUX);
+#endif
 }
 
-// Registers -> LDS.  Sub-tile `sub` of A sits at As + sub * BM * 8 and of B at
-// Bs + sub * (B tile size).  MX scales are widened to fp32 here, once per row
-// and stage, and stored group-major: Scf[group * (BNT + 32) + row] (the pad
-// puts the two lane halves' reads on different banks).
-template <bool MX, int BM, int BNT, int KS, int NTH>
-__device__ __forceinline__ void sstore(const Stage<MX, BM, BNT, KS, NTH> &st, u32x4_t *As, u32x4_t *Bs, float *Scf,
-                                       int tid)
+// Per-thread global offsets of one k-tile's A and B chunks (the k-tile's column
+// goes in the load's soffset).  The tiles travel from global memory straight
+// into LDS (buffer_load ... lds, 16 bytes per lane): load q of wave w fills
+// the 64 16-B slots [q*NTH + 64w, +64) of the tile, lane l the slot
+// q*NTH + 64w + l, so each lane's offset names the global chunk that the
+// swizzle puts in that slot.
+template <bool MX, int BM, int BNT, int NTH>
+struct Ptrs {
+    static constexpr int NAL = BM * 8 / NTH;                    // A loads per thread and k-tile
+    static constexpr int NBL = (MX ? BNT * 2 : BNT * 8) / NTH;  // B loads per thread and k-tile
+    static_assert(NAL >= 1 && NBL >= 1 && BM * 8 % NTH == 0 && (MX ? BNT * 2 : BNT * 8) % NTH == 0,
+                  "tile too small for the block");
+    uint32_t a[NAL];  // A: tile row (tid>>3) + (NTH/8)q, chunk (tid&7) ^ swizzle(row)
+    uint32_t b[NBL];  // B bf16: as A; MX: row (tid>>1) + (NTH/2)q, half (tid&1) ^ swizzle(row)
+    uint32_t s;       // MX: this thread's scale row within the blob
+};
+
+// The end of a k-tile: wait until at most N of this wave's memory loads are
+// outstanding (the N issued for the k-tile two ahead, so the next k-tile's
+// have landed in LDS) and its LDS operations are done, then meet the other
+// waves.  One asm statement with a memory clobber, so the compiler moves no
+// load or LDS access across the wait or the barrier.
+template <int N>
+__device__ __forceinline__ void stage_barrier()
 {
-    constexpr int NAL = Stage<MX, BM, BNT, KS, NTH>::NAL, NBL = Stage<MX, BM, BNT, KS, NTH>::NBL;
-    constexpr int BT = MX ? BNT * 2 : BNT * 8;  // 16-B slots of one B sub-tile
-#pragma unroll
-    for (int sub = 0; sub < KS; ++sub) {
-#pragma unroll
-        for (int q = 0; q < NAL; ++q)
-            As[sub * BM * 8 + swz((tid >> 3) + (NTH / 8) * q, tid & 7)] = st.a[sub * NAL + q];
-#pragma unroll
-        for (int q = 0; q < NBL; ++q) {
-            if (MX)
-                Bs[sub * BT + mx_slot((tid >> 1) + (NTH / 2) * q, tid & 1)] = st.b[sub * NBL + q];
-            else
-                Bs[sub * BT + swz((tid >> 3) + (NTH / 8) * q, tid & 7)] = st.b[sub * NBL + q];
-        }
-    }
-    if (MX && (BNT >= NTH || tid < BNT)) {
-        // The empty asm keeps the widening here, after the stage's other stores:
-        // left free, the compiler hoists it next to the load, and waiting for
-        // that load there waits for every load issued before it.
-        uint32_t sc = st.s;
-        asm volatile("" : "+v"(sc));
-#pragma unroll
-        for (int gi = 0; gi < 2 * KS; ++gi)
-            Scf[gi * (BNT + 32) + tid] = e8m0_f((sc >> (8 * gi)) & 0xffu);
-    }
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 // Map the 1-D block index to a work item so that each XCD gets a contiguous
@@ -186,6 +154,21 @@ template <int V>
 struct IC {
     static constexpr int value = V;
 };
+
+// run(IC<n>) for n = min(nms, N): one instance of the main loop per number of
+// MFMA row blocks, so the loop body has no branches on it
+template <int N, typename F>
+__device__ __forceinline__ void dispatch_rows(int nms, F &run)
+{
+    if constexpr (N == 0) {
+        run(IC<0>{});
+    } else {
+        if (nms >= N)
+            run(IC<N>{});
+        else
+            dispatch_rows<N - 1>(nms, run);
+    }
+}
 }  // namespace
 
 // MODE 1: GEMM1 + SwiGLU (A = x rows through perm, K = d, out H bf16 [R][I]).
@@ -199,7 +182,7 @@ struct IC {
 // and B alike, so every chunk is used once.  Lane half g then reads the 32
 // MXFP4 elements 32g..32g+31 -- 16 bytes, exactly one E8M0 scale group -- with
 // a single LDS read per k-tile.
-template <int MODE, bool MX, int BM, int BNT, int MINB, int KS, int WM, int NW>
+template <int MODE, bool MX, int BM, int BNT, int MINB, int WM, int NW>
 __global__ __launch_bounds__(64 * NW, MINB) void k_grouped_gemm(
     const uint64_t *__restrict__ ptrs, size_t off_w0, size_t off_w1, size_t off_s0, size_t off_s1,
     const int32_t *__restrict__ tiles, const int32_t *__restrict__ n_tiles,
@@ -209,15 +192,16 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_grouped_gemm(
     constexpr int NTH = 64 * NW, WN = NW / WM, WROWS = BM / WM, NMSMAX = WROWS / 32;
     constexpr int NCB = BNT / (32 * WN);  // 32-column MFMA blocks per wave
     static_assert(NW % WM == 0 && NCB >= (MODE == 1 ? 2 : 1) && NMSMAX >= 1, "wave layout");
-    constexpr int BT = MX ? BNT * 2 : BNT * 8;  // 16-B slots of one B sub-tile
-    // bf16 gate/up weights are streamed with non-temporal loads (each k-tile
-    // takes whole 128-B lines of a row; 800 -> 756 us for the 4096-token layer).
-    // MXFP4 k-tiles take 32 B of a line whose rest the next three k-tiles use,
-    // and the bf16 down GEMM got slower with them: default policy there.
-    constexpr int BAUX = (!MX && MODE == 1) ? 2 : 0;
-    __shared__ u32x4_t As[2][KS * BM * 8];
-    __shared__ u32x4_t Bs[2][KS * BT];
-    __shared__ float Scf[2][MX ? 2 * KS * (BNT + 32) : 4];
+    constexpr int BT = MX ? BNT * 2 : BNT * 8;  // 16-B slots of one B tile
+    using P = Ptrs<MX, BM, BNT, NTH>;
+    // loads issued per thread and k-tile: A and B chunks, and (MXFP4) the scale word
+    constexpr int NLD = P::NAL + P::NBL + (MX ? 1 : 0);
+    // Three LDS stages, each its own array: the compiler then sees which stage
+    // an in-flight global->LDS load writes, and an LDS read of one stage does
+    // not wait for the loads into another.
+    __shared__ u32x4_t A0[BM * 8], A1[BM * 8], A2[BM * 8];
+    __shared__ u32x4_t B0[BT], B1[BT], B2[BT];
+    __shared__ float Scf[2][MX ? 2 * (BNT + 32) : 4];
 
     const int item = xcd_item(blockIdx.x, *n_tiles * NT);
     if (item < 0)
@@ -237,16 +221,24 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_grouped_gemm(
     // MODE 1: this block's intermediate columns [n0, n0 + BNT/2); MODE 2: outputs [n0, n0 + BNT)
     const int n0 = nt * (MODE == 1 ? BNT / 2 : BNT);
 
-    Ptrs<MX, BM, BNT, NTH> p;
-#pragma unroll
-    for (int q = 0; q < Stage<MX, BM, BNT, 1, NTH>::NAL; ++q) {
-        const int row = min((tid >> 3) + (NTH / 8) * q, mrows - 1);
-        const size_t arow = MODE == 1 ? (size_t)(perm[rb + row] / k) : (size_t)row;  // from abase
-        p.a[q] = (uint32_t)(arow * lda * 2 + (tid & 7) * 16);
-    }
     // A: all of x (MODE 1; under 4 GiB, checked by the launcher) or the rows from
     // the tile's first on (MODE 2); B: the blob
     const size_t abytes = MODE == 1 ? (size_t)(R / k) * lda * 2 : (size_t)(R - rb) * lda * 2;
+    // Tile rows past the expert's last row load nothing: their offset lies past
+    // the A resource's size, so the buffer load returns zeros without a memory
+    // access (the range check takes the per-lane offset).  A resource of 2 GiB
+    // or more cannot place such an offset; its pad rows re-read the last row.
+    const bool a_oob = abytes < 0x80000000ull;
+    // load q of wave w fills tile rows 8 (q * NW + w) .. +7, lane l the slot of
+    // row (tid >> 3) + (NTH / 8) q at position l & 7: the chunk swz puts there
+    auto achunk = [](int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); };
+    P p;
+#pragma unroll
+    for (int q = 0; q < P::NAL; ++q) {
+        const int r = (tid >> 3) + (NTH / 8) * q, row = min(r, mrows - 1);
+        const size_t arow = MODE == 1 ? (size_t)(perm[rb + row] / k) : (size_t)row;  // from abase
+        p.a[q] = r < mrows || !a_oob ? (uint32_t)(arow * lda * 2 + achunk(r, tid & 7) * 16) : 0x80000000u;
+    }
     const rsrc_t ra = make_rsrc(A + (MODE == 1 ? 0 : (size_t)rb * lda), (uint32_t)min(abytes, (size_t)0xFFFFFFFFu));
     const rsrc_t rbs = make_rsrc((const void *)blob, blob_bytes);
     // weight row r of the block's B tile -> (section, scale section, matrix row)
@@ -262,20 +254,23 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_grouped_gemm(
     };
     if (MX) {
 #pragma unroll
-        for (int q = 0; q < Stage<MX, BM, BNT, 1, NTH>::NBL; ++q) {
+        for (int q = 0; q < P::NBL; ++q) {
             size_t so, sco;
-            const int r = brow((tid >> 1) + (NTH / 2) * q, so, sco);
-            p.b[q] = (uint32_t)(so + (size_t)r * (K / 2) + (tid & 1) * 16);
+            const int br = (tid >> 1) + (NTH / 2) * q;
+            const int r = brow(br, so, sco);
+            const int half = (tid & 1) ^ (((br >> 2) ^ (br >> 3)) & 1);  // mx_slot inverted
+            p.b[q] = (uint32_t)(so + (size_t)r * (K / 2) + half * 16);
         }
         size_t so, sco;
         const int r = brow(tid < BNT ? tid : 0, so, sco);
         p.s = (uint32_t)(sco + (size_t)r * (K / 32));
     } else {
 #pragma unroll
-        for (int q = 0; q < Stage<MX, BM, BNT, 1, NTH>::NBL; ++q) {
+        for (int q = 0; q < P::NBL; ++q) {
             size_t so, sco;
-            const int r = brow((tid >> 3) + (NTH / 8) * q, so, sco);
-            p.b[q] = (uint32_t)(so + (size_t)r * K * 2 + (tid & 7) * 16);
+            const int br = (tid >> 3) + (NTH / 8) * q;
+            const int r = brow(br, so, sco);
+            p.b[q] = (uint32_t)(so + (size_t)r * K * 2 + achunk(br, tid & 7) * 16);
         }
         p.s = 0;
     }
@@ -286,7 +281,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_grouped_gemm(
         brw[cb] = (l & 31) + (MODE == 1 ? (cb < NCB / 2 ? wn * (BNT / 2 / WN) + cb * 32
                                                        : BNT / 2 + wn * (BNT / 2 / WN) + (cb - NCB / 2) * 32)
                                         : wn * (BNT / WN) + cb * 32);
-    const int nk = K / (BK * KS);
+    const int nk = K / BK;
 
     // The pipelined main loop and epilogue, instantiated per number of MFMA
     // row blocks (0, 1, 2) this wave owns, so the loop body has no branches.
@@ -300,55 +295,96 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_grouped_gemm(
 #pragma unroll
                 for (int j = 0; j < 16; ++j)
                     acc[a][b][j] = 0.f;
-        Stage<MX, BM, BNT, KS, NTH> s0, s1;
-        gload<BAUX>(s0, p, ra, rbs, 0, tid);
-        gload<BAUX>(s1, p, ra, rbs, 1, tid);
-        sstore(s0, As[0], Bs[0], Scf[0], tid);
-        __syncthreads();
-        // NXT holds k-tile kt+1 (loaded one iteration ago); FRE is free and
-        // receives k-tile kt+2.  Two copies of the body alternate the roles so
-        // both stages stay in named registers.  Loads and stores are issued on
-        // every iteration (nk is even and >= 2; past the end the last k-tile is
-        // re-read into a buffer nobody reads): branch-free, the compiler's
-        // load counters wait only for the older stage, which keeps two k-tiles
-        // of loads in flight.
-#define ECF_GEMM_BODY(KT, NXT, FRE)                                                                  \
-    {                                                                                               \
-        const int cur = (KT) & 1;                                                                   \
-        gload<BAUX>(FRE, p, ra, rbs, min((KT) + 2, nk - 1), tid);                                   \
-        if (NMS > 0) {                                                                              \
-            _Pragma("unroll") for (int sub = 0; sub < KS; ++sub)                                    \
-            {                                                                                       \
-                const u32x4_t *Asb = As[cur] + sub * BM * 8, *Bsb = Bs[cur] + sub * BT;             \
-                float bsc[NCB];                                                                     \
-                if (MX) {                                                                           \
-                    _Pragma("unroll") for (int cb = 0; cb < NCB; ++cb)                              \
-                        bsc[cb] = Scf[cur][(sub * 2 + g) * (BNT + 32) + brw[cb]];                   \
-                }                                                                                   \
-                _Pragma("unroll") for (int ks = 0; ks < BK / 16; ++ks)                              \
-                {                                                                                   \
-                    const int kc = 4 * g + ks;                                                      \
-                    bf16x8_t af[NMSMAX], bfr[NCB];                                                  \
-                    _Pragma("unroll") for (int ms = 0; ms < NMS; ++ms) af[ms] =                    \
-                        frag_bf16(Asb, wm * WROWS + ms * 32 + (l & 31), kc);                        \
-                    _Pragma("unroll") for (int cb = 0; cb < NCB; ++cb) bfr[cb] =                    \
-                        MX ? cvt_mx8(reinterpret_cast<const uint32_t *>(Bsb)[mx_slot(brw[cb], g) * 4 + ks], \
-                                     bsc[cb])                                                       \
-                           : frag_bf16(Bsb, brw[cb], kc);                                           \
-                    _Pragma("unroll") for (int ms = 0; ms < NMS; ++ms)                              \
-                        _Pragma("unroll") for (int cb = 0; cb < NCB; ++cb) acc[ms][cb] =            \
-                            __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ms], bfr[cb], acc[ms][cb], 0, 0, 0); \
-                }                                                                                   \
-            }                                                                                       \
-        }                                                                                           \
-        sstore(NXT, As[cur ^ 1], Bs[cur ^ 1], Scf[cur ^ 1], tid);                                   \
-        __syncthreads();                                                                            \
-    }
-        for (int kt = 0; kt < nk; kt += 2) {
-            ECF_GEMM_BODY(kt, s1, s0)
-            ECF_GEMM_BODY(kt + 1, s0, s1)
+        // MXFP4 scale words travel through registers two k-tiles ahead and are
+        // widened into Scf for the next k-tile at the end of each k-tile.
+        auto sload = [&](int kt) -> uint32_t {
+            return MX ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rbs, p.s, kt * 2, 0) : 0u;
+        };
+        auto sput = [&](uint32_t sc, float *dst) __attribute__((always_inline)) {
+            if (MX && (BNT >= NTH || tid < BNT)) {
+                // The empty asm keeps the widening here, after the k-tile's
+                // MFMAs: left free, the compiler hoists it next to the load, and
+                // waiting for that load there waits for every load issued before it.
+                asm volatile("" : "+v"(sc));
+#pragma unroll
+                for (int gi = 0; gi < 2; ++gi)
+                    dst[gi * (BNT + 32) + tid] = e8m0_f((sc >> (8 * gi)) & 0xffu);
+            }
+        };
+        // k-tile kt of A and B into LDS stage (Ad, Bd).  bf16 gate/up weights are
+        // streamed with non-temporal loads (each k-tile takes whole 128-B lines
+        // of a row; 800 -> 756 us for the 4096-token layer).  MXFP4 k-tiles take
+        // 32 B of a line whose rest the next three k-tiles use, and the bf16 down
+        // GEMM got slower with them: default policy there.
+        auto dma_tile = [&](u32x4_t *Ad, u32x4_t *Bd, int kt) __attribute__((always_inline)) {
+            const int col = kt * BK;
+#pragma unroll
+            for (int q = 0; q < P::NAL; ++q)
+                lds_load16<0>(ra, Ad + q * NTH + 64 * w, p.a[q], col * 2);
+#pragma unroll
+            for (int q = 0; q < P::NBL; ++q)
+                lds_load16<(!MX && MODE == 1) ? 2 : 0>(rbs, Bd + q * NTH + 64 * w, p.b[q], MX ? col / 2 : col * 2);
+        };
+        dma_tile(A0, B0, 0);
+        const uint32_t sc0 = sload(0);
+        dma_tile(A1, B1, min(1, nk - 1));
+        uint32_t sc_next = sload(min(1, nk - 1));
+        sput(sc0, Scf[0]);
+        stage_barrier<NLD>();
+        // One k-tile: the loads of k-tile kt+2 go out first (into the stage
+        // k-tile kt-1 used), then the MFMAs of k-tile kt, then the wait for
+        // k-tile kt+1.  Past the end the last k-tile is loaded again into a stage
+        // nobody reads, so every k-tile issues the same NLD loads.
+        auto body = [&](int kt, const u32x4_t *Ac, const u32x4_t *Bc, u32x4_t *An, u32x4_t *Bn)
+                        __attribute__((always_inline)) {
+            const int cur = kt & 1;
+            dma_tile(An, Bn, min(kt + 2, nk - 1));
+            const uint32_t sc_new = sload(min(kt + 2, nk - 1));
+            // issue them here, two k-tiles ahead of their use (the scheduler
+            // would otherwise sink them below the MFMAs)
+            asm volatile("" ::: "memory");
+            if (NMS > 0) {
+                float bsc[NCB];
+                if (MX) {
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb)
+                        bsc[cb] = Scf[cur][g * (BNT + 32) + brw[cb]];
+                }
+#pragma unroll
+                for (int ks = 0; ks < BK / 16; ++ks) {
+                    const int kc = 4 * g + ks;
+                    bf16x8_t af[NMSMAX], bfr[NCB];
+#pragma unroll
+                    for (int ms = 0; ms < NMS; ++ms)
+                        af[ms] = frag_bf16(Ac, wm * WROWS + ms * 32 + (l & 31), kc);
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb)
+                        bfr[cb] = MX ? cvt_mx8(reinterpret_cast<const uint32_t *>(Bc)[mx_slot(brw[cb], g) * 4 + ks], bsc[cb])
+                                     : frag_bf16(Bc, brw[cb], kc);
+#pragma unroll
+                    for (int ms = 0; ms < NMS; ++ms)
+#pragma unroll
+                        for (int cb = 0; cb < NCB; ++cb)
+                            acc[ms][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ms], bfr[cb], acc[ms][cb], 0, 0, 0);
+                }
+            }
+            sput(sc_next, Scf[cur ^ 1]);
+            sc_next = sc_new;
+            stage_barrier<NLD>();
+        };
+        // stage of k-tile kt = kt % 3; each call names its arrays statically
+        int kt = 0;
+        for (; kt + 3 <= nk; kt += 3) {
+            body(kt, A0, B0, A2, B2);
+            body(kt + 1, A1, B1, A0, B0);
+            body(kt + 2, A2, B2, A1, B1);
         }
-#undef ECF_GEMM_BODY
+        if (kt < nk)
+            body(kt, A0, B0, A2, B2);
+        if (kt + 1 < nk)
+            body(kt + 1, A1, B1, A0, B0);
+        // the last loads (of k-tiles nobody reads) land before the wave moves on
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         // epilogue: a lane holds rows (j/4)*8 + (l/32)*4 + j%4 of column l%32 of each fragment
 #pragma unroll
         for (int ms = 0; ms < NMS; ++ms) {
@@ -376,31 +412,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_grouped_gemm(
     // MFMA row blocks of this wave that hold real rows (uniform over the wave)
     // (with WM = 1 a block of 65..96 rows runs 4 row blocks: one wasted, one fewer instance)
     const int nms = __builtin_amdgcn_readfirstlane(max(0, min(NMSMAX, (mrows - wm * WROWS + 31) / 32)));
-    static_assert(NMSMAX <= 5, "row-block instances below cover up to 5");
-    if constexpr (NMSMAX >= 5) {
-        if (nms >= 5) {
-            run(IC<NMSMAX>{});
-            return;
-        }
-    }
-    if constexpr (NMSMAX >= 4) {
-        if (nms == 4) {
-            run(IC<4>{});
-            return;
-        }
-    }
-    if constexpr (NMSMAX >= 3) {
-        if (nms == 3) {
-            run(IC<3>{});
-            return;
-        }
-    }
-    if (nms == 2)
-        run(IC<2>{});
-    else if (nms == 1)
-        run(IC<1>{});
-    else
-        run(IC<0>{});
+    dispatch_rows<NMSMAX>(nms, run);
 }
 
 // ---------------------------------------------------------------------------------
@@ -418,11 +430,13 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_grouped_gemm(
 // (256-row tiles with 8 waves were 5% faster than 4 waves on 128 x 256).  Two-sub-tile
 // stages, a 1 x 4 wave layout, three blocks per CU, expanding MXFP4 to bf16 once
 // at the LDS store, 4 waves on 256 x 256 and 8 waves on 128 x 256 were each
-// slower or spilled registers.
+// slower or spilled registers.  With the global->LDS pipeline: 4 waves of
+// 320 x 64 each (one wave per SIMD, 512 registers) spilled; pinning each A
+// fragment's LDS read two row blocks ahead of its MFMAs with scheduling
+// groups made MXFP4 GEMM1 slower (2060 -> 2235 us).
 #ifndef ECF_BF16_BNT
 #define ECF_BF16_BNT 256
 #define ECF_BF16_MINB 1
-#define ECF_BF16_KS 1
 #define ECF_BF16_WM 2
 #endif
 #ifndef ECF_BF16_NW
@@ -431,7 +445,6 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_grouped_gemm(
 #ifndef ECF_MX_BNT
 #define ECF_MX_BNT 256
 #define ECF_MX_MINB 1
-#define ECF_MX_KS 1
 #define ECF_MX_WM 2
 #endif
 #ifndef ECF_MX_NW
@@ -451,18 +464,17 @@ int launch_prefill_gemm1(const ecf_shape &s, const ExpertTables &ex, const Route
                          "be under 4 GiB", T, s.hidden, ex.lay.bytes);
     const int nblk = max_tiles(s, T) * NT;
     ProfScope p("prefill_gemm1", st);
-#define ECF_G1(MXV, BNV, MBV, KSV, WMV, NWV)                                                               \
-    hipLaunchKernelGGL((k_grouped_gemm<1, MXV, (MXV) ? ECF_MX_BM : kPrefillMT, BNV, MBV, KSV, WMV, NWV>), dim3(nblk), \
+#define ECF_G1(MXV, BNV, MBV, WMV, NWV)                                                                     \
+    hipLaunchKernelGGL((k_grouped_gemm<1, MXV, (MXV) ? ECF_MX_BM : kPrefillMT, BNV, MBV, WMV, NWV>), dim3(nblk), \
                        dim3(64 * (NWV)), 0, st, ex.ptrs,                                                     \
                        ex.lay.off[0], ex.lay.off[1], ex.lay.off[3], ex.lay.off[4], o.tiles, o.n_tiles,         \
                        o.offsets, o.perm, (const uint16_t *)x, s.hidden, s.inter, s.hidden, s.top_k,         \
                        s.n_experts, T * s.top_k, NT, (uint32_t)ex.lay.bytes, (void *)H)
-    // K = d; the main loop takes an even number of stages of KS sub-tiles: d % (128 * KS) == 0
-    // (d is a multiple of 256)
+    // K = d, a multiple of the 64-element k-tile
     if (mx)
-        ECF_G1(true, ECF_MX_BNT, ECF_MX_MINB, ECF_MX_KS, ECF_MX_WM, ECF_MX_NW);
+        ECF_G1(true, ECF_MX_BNT, ECF_MX_MINB, ECF_MX_WM, ECF_MX_NW);
     else
-        ECF_G1(false, ECF_BF16_BNT, ECF_BF16_MINB, ECF_BF16_KS, ECF_BF16_WM, ECF_BF16_NW);
+        ECF_G1(false, ECF_BF16_BNT, ECF_BF16_MINB, ECF_BF16_WM, ECF_BF16_NW);
 #undef ECF_G1
     ECF_HIP_CHECK(hipGetLastError());
     return ECF_OK;
@@ -478,25 +490,17 @@ int launch_prefill_gemm2(const ecf_shape &s, const ExpertTables &ex, const Route
         return set_error(ECF_EUNSUPPORTED, "prefill path: one expert blob (%zu B) must be under 4 GiB", ex.lay.bytes);
     const int nblk = max_tiles(s, T) * NT;
     ProfScope p("prefill_gemm2", st);
-#define ECF_G2(MXV, BNV, MBV, KSV, WMV, NWV)                                                               \
-    hipLaunchKernelGGL((k_grouped_gemm<2, MXV, (MXV) ? ECF_MX_BM : kPrefillMT, BNV, MBV, KSV, WMV, NWV>), dim3(nblk), \
+#define ECF_G2(MXV, BNV, MBV, WMV, NWV)                                                                     \
+    hipLaunchKernelGGL((k_grouped_gemm<2, MXV, (MXV) ? ECF_MX_BM : kPrefillMT, BNV, MBV, WMV, NWV>), dim3(nblk), \
                        dim3(64 * (NWV)), 0, st, ex.ptrs,                                                     \
                        ex.lay.off[2], ex.lay.off[2], ex.lay.off[5], ex.lay.off[5], o.tiles, o.n_tiles,         \
                        o.offsets, o.perm, H, s.inter, s.hidden, s.inter, s.top_k, s.n_experts, T * s.top_k,  \
                        NT, (uint32_t)ex.lay.bytes, (void *)Y)
-    // K = I; the main loop takes an even number of stages: two-sub-tile stages
-    // only when I % 256 == 0 (I % 128 == 0 holds on this path)
-    if (mx) {
-        if (s.inter % (128 * ECF_MX_KS) == 0)
-            ECF_G2(true, ECF_MX_BNT, ECF_MX_MINB, ECF_MX_KS, ECF_MX_WM, ECF_MX_NW);
-        else
-            ECF_G2(true, ECF_MX_BNT, ECF_MX_MINB, 1, ECF_MX_WM, ECF_MX_NW);
-    } else {
-        if (s.inter % (128 * ECF_BF16_KS) == 0)
-            ECF_G2(false, ECF_BF16_BNT, ECF_BF16_MINB, ECF_BF16_KS, ECF_BF16_WM, ECF_BF16_NW);
-        else
-            ECF_G2(false, ECF_BF16_BNT, ECF_BF16_MINB, 1, ECF_BF16_WM, ECF_BF16_NW);
-    }
+    // K = I, a multiple of the 64-element k-tile on this path
+    if (mx)
+        ECF_G2(true, ECF_MX_BNT, ECF_MX_MINB, ECF_MX_WM, ECF_MX_NW);
+    else
+        ECF_G2(false, ECF_BF16_BNT, ECF_BF16_MINB, ECF_BF16_WM, ECF_BF16_NW);
 #undef ECF_G2
     ECF_HIP_CHECK(hipGetLastError());
     return ECF_OK;
