@@ -76,20 +76,74 @@ def bench_hbm(torch, ecf, reps=10):
         ev1.record()
         torch.cuda.synchronize()
         out[f"{name}_GBps"] = nbytes * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    # the MFMA rate under a GEMM-like load: bf16 MFMAs only, from registers, with
+    # operands that change from one MFMA to the next (libecf's ecf_mfma_rate)
+    mf = {}
+    for bpc in (1, 2):
+        st = torch.cuda.current_stream().cuda_stream
+        ecf.ecf_mfma_rate(2000, bpc, sink.data_ptr(), st)  # warm-up
+        ts = []
+        for _ in range(5):
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record()
+            flop = ecf.ecf_mfma_rate(20000, bpc, sink.data_ptr(), st)
+            ev1.record()
+            torch.cuda.synchronize()
+            ts.append(ev0.elapsed_time(ev1) * 1e-3)
+        mf[bpc] = flop / sorted(ts)[len(ts) // 2] / 1e12
+    out["mfma_bf16_TFLOPs"] = max(mf.values())
+    out["mfma_bf16_TFLOPs_by_waves_per_simd"] = {str(k): v for k, v in mf.items()}
+    out["mfma_bf16_peak_TFLOPs"] = BF16_PEAK_TFLOPS
     del a, b, c, sink
     torch.cuda.empty_cache()
     out["peak_GBps"] = HBM_PEAK_GBS
     log(f"hbm: plain read {out['read_GBps']:.0f} GB/s, device copy {out['copy_GBps']:.0f} GB/s "
-        f"(read+write), datasheet peak {HBM_PEAK_GBS:.0f}")
+        f"(read+write), datasheet peak {HBM_PEAK_GBS:.0f}; bf16 MFMA-only loop {out['mfma_bf16_TFLOPs']:.0f} "
+        f"TFLOP/s (datasheet {BF16_PEAK_TFLOPS:.0f})")
     return out
+
+
+def one_launch_read_us(torch, ecf, nbytes, reps=5, launches=10):
+    """Time per launch of ecf_stream_read over nbytes (rounded down to 16 B):
+    the floor for any single kernel that streams that many bytes from HBM,
+    launch and ramp included.  The launches are captured in one HIP graph, as
+    the decode steps are, and replayed back to back; each reads a different
+    region of a 4 GiB buffer whose pages have all been written, so none is
+    served from the 256 MB last-level cache.  Median over repeats."""
+    span = 1 << 32
+    nbytes = max(16, nbytes // 16 * 16)
+    buf = torch.empty(span, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    slots = max(1, span // nbytes)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(launches):
+            ecf.ecf_stream_read(buf.data_ptr() + (i % slots) * nbytes, nbytes, sink.data_ptr(), stream.cuda_stream)
+    ts = []
+    with torch.cuda.stream(stream):
+        for r in range(reps + 1):
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            g.replay()
+            ev1.record(stream)
+            stream.synchronize()
+            if r >= 1:
+                ts.append(1e3 * ev0.elapsed_time(ev1) / launches)
+    del g, buf, sink
+    torch.cuda.empty_cache()
+    return sorted(ts)[len(ts) // 2]
 
 
 def bench_vendor_gemm(torch, reps=5):
     """Calibration, not part of the layer: torch.bmm (the ROCm BLAS libraries)
     on the prefill layers' per-expert GEMM shapes with every expert holding
     exactly R/E rows and dense bf16 weights (no ragged tiles, no MXFP4
-    expansion), plus one large square GEMM -- what the vendor's GEMMs reach on
-    this GPU for the same work.  Right operands are contiguous [E, K, N]."""
+    expansion), plus one large square GEMM and one large dense torch.mm with
+    the MXFP4 GEMM1's flop -- what the vendor's GEMMs reach on this GPU for
+    the same work.  Right operands of bmm are contiguous [E, K, N]."""
     shapes = {  # name: (batch, M, K, N)
         "square_8192": (1, 8192, 8192, 8192),
         "prefill_bf16_gemm1": (256, 96, 4096, 2048),    # 4096 tokens x top-6 / 256 experts; [gate|up]
@@ -115,7 +169,25 @@ def bench_vendor_gemm(torch, reps=5):
                      "mfma_frac": tf / BF16_PEAK_TFLOPS}
         del a, b, c
     torch.cuda.empty_cache()
-    log("vendor bmm: " + ", ".join(f"{k} {v['us']:.0f} us ({v['tflops']:.0f} TF)" for k, v in out.items()))
+    # one large dense GEMM with the MXFP4 prefill GEMM1's flop (torch.mm)
+    m, kk, n = 65536, 4096, 4096
+    a = torch.randn(m, kk, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, kk, device="cuda", dtype=torch.bfloat16)
+    c = torch.mm(a, b.t())
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(reps):
+        torch.mm(a, b.t(), out=c)
+    ev1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * ev0.elapsed_time(ev1) / reps
+    tf = 2.0 * m * kk * n / (us * 1e-6) / 1e12
+    out["dense_mm_65536x4096x4096"] = {"batch": 1, "M": m, "K": kk, "N": n, "us": us, "tflops": tf,
+                                       "mfma_frac": tf / BF16_PEAK_TFLOPS}
+    del a, b, c
+    torch.cuda.empty_cache()
+    log("vendor bmm/mm: " + ", ".join(f"{k} {v['us']:.0f} us ({v['tflops']:.0f} TF)" for k, v in out.items()))
     return out
 
 
@@ -231,9 +303,18 @@ def bench_decode(torch, ecf, syn, Ts, steps, warmup, n_batches=64, use_graph=Tru
             layer_hbm_frac=layer_bytes / (ms / steps * 1e-3) / 1e9 / HBM_PEAK_GBS,
             gateup_bytes=gu_bytes, gateup_avg_us=gu_us, gateup_GBps=gu_bytes / (gu_us * 1e-6) / 1e9,
             kernels=kern, graph=use_graph)
+        # the same bytes read by one plain streaming kernel: the floor for the
+        # whole layer, which is a chain of dependent kernels
+        if layer_bytes < (1 << 31):
+            floor = one_launch_read_us(torch, ecf, int(layer_bytes))
+            results[T]["one_launch_read_us"] = floor
+            results[T]["layer_time_over_one_launch_read"] = ms / steps * 1e3 / floor
+        floor_s = (f", one plain read of the layer's bytes {results[T]['one_launch_read_us']:.1f} us"
+                   if "one_launch_read_us" in results[T] else "")
         log(f"decode {w_dtype} T={T}: {ms / steps * 1e3:.1f} us/step (median {per_step[steps // 2]:.1f}), "
             f"{results[T]['tokens_per_s']:.0f} tok/s, "
-            f"U={U_avg:.1f}, layer {results[T]['layer_GBps']:.0f} GB/s, gate/up {results[T]['gateup_GBps']:.0f} GB/s")
+            f"U={U_avg:.1f}, layer {results[T]['layer_GBps']:.0f} GB/s, gate/up {results[T]['gateup_GBps']:.0f} GB/s"
+            f"{floor_s}")
         del graphs
     def gpu_run(x_cpu):
         """One eager forward of the layer on x (host tensor); routing and output on the host."""

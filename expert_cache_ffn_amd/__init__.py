@@ -20,5 +20,5 @@ from ._lib import (  # noqa: F401
     ecf_cache_available, ecf_cache_slot_of, ecf_cache_get_stats, ecf_cache_resize,
     prefetch_layer, moe_layer_forward, moe_layer_forward_noalloc, ecf_noalloc_scratch_bytes,
     ecf_host_experts, ecf_bandwidth_profile,
-    ecf_profile_enable, ecf_profile_get_all, ecf_profile_reset, ecf_stream_read,
+    ecf_profile_enable, ecf_profile_get_all, ecf_profile_reset, ecf_stream_read, ecf_mfma_rate,
 )

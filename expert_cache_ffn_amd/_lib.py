@@ -26,7 +26,7 @@ EXPORTS = [
     "ecf_cache_available", "ecf_cache_slot_of", "ecf_cache_get_stats", "ecf_cache_resize",
     "prefetch_layer", "moe_layer_forward", "moe_layer_forward_noalloc", "ecf_noalloc_scratch_bytes",
     "ecf_host_experts", "ecf_bandwidth_profile", "ecf_profile_enable",
-    "ecf_profile_get", "ecf_profile_reset", "ecf_stream_read",
+    "ecf_profile_get", "ecf_profile_reset", "ecf_stream_read", "ecf_mfma_rate",
 ]
 
 
@@ -128,6 +128,8 @@ def lib():
         L.ecf_profile_reset.argtypes, L.ecf_profile_reset.restype = [], c_int32
         L.ecf_stream_read.argtypes = [c_void_p, c_size_t, c_void_p, c_void_p]
         L.ecf_stream_read.restype = c_int32
+        L.ecf_mfma_rate.argtypes = [c_int32, c_int32, c_void_p, c_void_p, POINTER(c_double)]
+        L.ecf_mfma_rate.restype = c_int32
         _lib = L
     return _lib
 
@@ -293,6 +295,14 @@ def ecf_profile_get_all() -> dict:
 
 def ecf_stream_read(d_buf, nbytes, d_sink, stream=0):
     return _check(lib().ecf_stream_read(int(d_buf) or None, int(nbytes), int(d_sink) or None, int(stream) or None))
+
+
+def ecf_mfma_rate(iters, blocks_per_cu, d_sink, stream=0):
+    """Enqueue the MFMA-rate measurement kernel; returns the flop it performs."""
+    flop = c_double(0.0)
+    _check(lib().ecf_mfma_rate(int(iters), int(blocks_per_cu), int(d_sink) or None, int(stream) or None,
+                               ctypes.byref(flop)))
+    return flop.value
 
 
 def ecf_profile_reset():

@@ -349,6 +349,19 @@ int ecf_profile_reset(void);
  */
 int ecf_stream_read(const void *d_buf, size_t bytes, uint32_t *d_sink, void *stream);
 
+/* Measurement: enqueue on `stream` a kernel that runs only bf16 MFMAs
+ * (v_mfma_f32_32x32x16_bf16, 32x32x16 per instruction) from registers on
+ * every compute unit: blocks_per_cu blocks of 4 waves each, `iters` rounds of
+ * eight independent MFMAs per wave, on pseudo-random operands that change
+ * from one MFMA to the next.  *flop receives the flop it performs (host
+ * value, known at enqueue); timing it with events around the launch gives
+ * the MFMA rate the GPU sustains under that load, the yardstick for the
+ * grouped GEMMs' MFMA fraction (MI355X datasheet: 2.5 PFLOP/s dense bf16).
+ * d_sink: one device float, written only in a case that cannot occur.
+ * ECF_EINVAL if iters <= 0, blocks_per_cu is outside 1..8, or a pointer is
+ * NULL. */
+int ecf_mfma_rate(int32_t iters, int32_t blocks_per_cu, float *d_sink, void *stream, double *flop);
+
 #ifdef __cplusplus
 }
 #endif

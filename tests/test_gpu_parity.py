@@ -423,3 +423,20 @@ def test_stream_read_xor():
         ecf.ecf_stream_read(buf.data_ptr(), 4 * n_words, sink.data_ptr())
         torch.cuda.synchronize()
         assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(np.bitwise_xor.reduce(words))
+
+
+def test_mfma_rate_counts_and_runs():
+    """The MFMA-rate yardstick reports the flop it launches (4 waves per block,
+    8 MFMAs of 32x32x16 per round) and runs to completion at a plausible rate."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    flop = ecf.ecf_mfma_rate(4000, 2, sink.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    ev1.record()
+    torch.cuda.synchronize()
+    assert flop == cus * 2 * 4 * 4000 * 8 * 2.0 * 32 * 32 * 16
+    assert float(sink.item()) == 0.0
+    tflops = flop / (ev0.elapsed_time(ev1) * 1e-3) / 1e12
+    assert 100.0 < tflops < 2600.0

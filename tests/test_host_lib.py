@@ -306,6 +306,14 @@ def test_stream_read_argument_checks():
         assert ei.value.code == ecf.ECF_EINVAL
 
 
+
+def test_mfma_rate_argument_checks():
+    """The MFMA-rate yardstick rejects bad arguments before touching a GPU."""
+    for iters, bpc, sink in ((0, 1, 64), (-5, 1, 64), (10, 0, 64), (10, 9, 64), (10, 1, 0)):
+        with pytest.raises(ecf.EcfError) as e:
+            ecf.ecf_mfma_rate(iters, bpc, sink)
+        assert e.value.code == ecf.ECF_EINVAL
+
 def test_bench_refuses_more_than_one_gpu():
     """bench.py measures one GPU: --gpus above 1 exits with status 2 and says so,
     before anything touches a GPU."""
