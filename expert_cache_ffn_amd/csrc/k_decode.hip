@@ -769,24 +769,36 @@ __global__ __launch_bounds__(256) void k_combine(
     if (c >= d)
         return;
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-    for (int j = 0; j < k; ++j) {
-        const int p = srow[j];
-        if (p < 0)
-            continue;
-        const float g = sg[j];
-        float4 y;
-        if (NT_Y) {
-            const uint4 yu = ld_nt16(Y + (size_t)p * d + c);
-            y = make_float4(__uint_as_float(yu.x), __uint_as_float(yu.y), __uint_as_float(yu.z),
-                            __uint_as_float(yu.w));
-        } else {
-            y = *reinterpret_cast<const float4 *>(Y + (size_t)p * d + c);
+    // Eight rows at a time: all eight loads are issued before the first is
+    // used (a skipped row -- not evaluated here, or past k -- loads row 0 and
+    // is then left out by a select, so no load sits behind a branch), then the
+    // rows are added in ascending j.  (With a branch per row the compiler
+    // waited for each row's load before issuing the next: decode at one token
+    // 49.9-51.6 -> 48.6 us, at four 113 -> 111 us.)
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        float4 y[8];
+        int p[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            p[u] = j0 + u < k ? srow[j0 + u] : -1;
+            const size_t at = (size_t)(p[u] < 0 ? 0 : p[u]) * d + c;
+            if (NT_Y) {
+                const uint4 yu = ld_nt16(Y + at);
+                y[u] = make_float4(__uint_as_float(yu.x), __uint_as_float(yu.y), __uint_as_float(yu.z),
+                                   __uint_as_float(yu.w));
+            } else {
+                y[u] = *reinterpret_cast<const float4 *>(Y + at);
+            }
         }
-        s.x = fmaf(g, y.x, s.x);
-        s.y = fmaf(g, y.y, s.y);
-        s.z = fmaf(g, y.z, s.z);
-        s.w = fmaf(g, y.w, s.w);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const bool use = p[u] >= 0;
+            const float g = use ? sg[j0 + u] : 0.f;
+            s.x = use ? fmaf(g, y[u].x, s.x) : s.x;
+            s.y = use ? fmaf(g, y[u].y, s.y) : s.y;
+            s.z = use ? fmaf(g, y[u].z, s.z) : s.z;
+            s.w = use ? fmaf(g, y[u].w, s.w) : s.w;
+        }
     }
     const size_t o = (size_t)t * d + c;
     if (host_part) {
