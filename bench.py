@@ -305,7 +305,9 @@ def bench_decode(torch, ecf, syn, Ts, steps, warmup, n_batches=64, use_graph=Tru
             kernels=kern, graph=use_graph)
         # the same bytes read by one plain streaming kernel: the floor for the
         # whole layer, which is a chain of dependent kernels
-        if layer_bytes < (1 << 31):
+        # (not in the host-input mode used for hardware-counter passes: the floor
+        # runs torch kernels, which that mode keeps out of the profiled process)
+        if layer_bytes < (1 << 31) and not host_inputs:
             floor = one_launch_read_us(torch, ecf, int(layer_bytes))
             results[T]["one_launch_read_us"] = floor
             results[T]["layer_time_over_one_launch_read"] = ms / steps * 1e3 / floor
