@@ -970,6 +970,12 @@ def main():
                                                     host_inputs=args.host_inputs)
     if "vendor" in wl:
         also["vendor_bmm_calibration"] = bench_vendor_gemm(torch)
+    # each prefill layer's MFMA rate against what the MFMA pipes sustain on this
+    # GPU with nothing else to do (ecf_mfma_rate), beside the datasheet fraction
+    if hbm:
+        for key in ("prefill_bf16_T4096", "prefill_mxfp4_T8192"):
+            if key in also:
+                also[key]["mfma_frac_of_mfma_only_loop"] = also[key]["tflops"] / hbm["mfma_bf16_TFLOPs"]
     if sample is not None and not args.no_cpu_baseline:
         log("cpu baseline: oracle on sampled decode batches")
         cpu = cpu_baseline_decode(torch, syn, sample)
