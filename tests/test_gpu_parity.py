@@ -54,6 +54,22 @@ def test_decode_bf16_full_size(decode_cases, T):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("T,path", [(64, ecf.ECF_PATH_DECODE), (65, ecf.ECF_PATH_PREFILL)])
+def test_auto_path_boundary_full_size(decode_cases, T, path):
+    """The forward call picks the decode GEMVs up to 64 tokens and the grouped
+    GEMMs above (bf16 weights, I % 128 == 0); both sides of the switch on the
+    full decode layer (64 tokens: experts with up to ~6 rows, several 2-row
+    passes of the GEMVs) against the oracle."""
+    cfg = decode_cases
+    say(f"case: auto path full size T={T}")
+    c = Case(cfg, T, gen_device="cuda")
+    res = c.run()
+    assert res["stats"]["path"] == path
+    compare(res, c.oracle(), TOL["bf16"], f"auto path T={T}")
+    del c
+    torch.cuda.empty_cache()
+
+
 # ---- edge cases on small shapes -------------------------------------------------------
 
 @pytest.mark.parametrize("path", [ecf.ECF_PATH_DECODE, ecf.ECF_PATH_PREFILL])
@@ -311,7 +327,7 @@ def test_decode_mxfp4_small(T, E, k, I):
     assert MX_DECODE_TOL <= TOL["mxfp4"]
 
 
-@pytest.mark.parametrize("T", [1, 16])
+@pytest.mark.parametrize("T", [1, 16, 64])
 def test_decode_mxfp4_full_size(T):
     """The decode layer shape (d 4096, 256 experts, I 1024, top-6) with MXFP4 experts."""
     import dataclasses
