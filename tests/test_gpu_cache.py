@@ -165,7 +165,7 @@ def _layer_experts(cs, cfg, l):
     return out
 
 
-@pytest.mark.parametrize("T", [1, 4, 16])
+@pytest.mark.parametrize("T", [1, 4, 16, 64])
 def test_cached_decode_full_shape_two_layers(T):
     """d 4096, 256 experts, I 1024, top-6, slots = 37% of the (2-layer) pool,
     Zipf(1.1) routing, q* at B_P/B_H = 0.4, host blobs aliased 32 ways: every
