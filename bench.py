@@ -912,8 +912,8 @@ def main():
                          "the same layers with MXFP4 experts; vendor: torch.bmm on the prefill GEMM shapes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--cached-steps", type=int, default=12)
-    ap.add_argument("--cached-warmup", type=int, default=None, help="cached decode warm-up steps (default: --cached-steps)")
+    ap.add_argument("--cached-steps", type=int, default=32, help="cached decode timed steps per policy and batch size")
+    ap.add_argument("--cached-warmup", type=int, default=16, help="cached decode warm-up steps (the LRU fills)")
     ap.add_argument("--policies", default=",".join(POLICIES), help="policies the 'policies' workload compares")
     ap.add_argument("--cached-tokens", default="1,4,16", help="cached-decode batch sizes (cached, policies)")
     ap.add_argument("--calib-copy", action="store_true",
