@@ -40,20 +40,15 @@ __device__ __forceinline__ uint64_t dpp64(uint64_t x)
 
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x)
 {
-    x = umax64(x, dpp64<kDppXor1>(x));
-    x = umax64(x, dpp64<kDppXor2>(x));
-    x = umax64(x, dpp64<kDppHalfMirror>(x));
-    x = umax64(x, dpp64<kDppMirror>(x));
-    uint64_t r = 0;
-#pragma unroll
-    for (int row = 0; row < 4; ++row) {
-        const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 16 * row);
-        const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)x, 16 * row);
-        r = umax64(r, ((uint64_t)hi << 32) | lo);
-    }
-    return r;
+    x = max(x, dpp32<kDppXor1>(x));
+    x = max(x, dpp32<kDppXor2>(x));
+    x = max(x, dpp32<kDppHalfMirror>(x));
+    x = max(x, dpp32<kDppMirror>(x));
+    const uint32_t r0 = __builtin_amdgcn_readlane((int)x, 0), r1 = __builtin_amdgcn_readlane((int)x, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane((int)x, 32), r3 = __builtin_amdgcn_readlane((int)x, 48);
+    return max(max(r0, r1), max(r2, r3));
 }
 
 __device__ __forceinline__ float wave_sum_f32(float x)
@@ -174,7 +169,10 @@ __device__ __forceinline__ float key_value(uint64_t key)
 // ---------------------------------------------------------------------------------
 // Top-k of one token's logits by one wave.  MAXS = logits held per lane.  Each of
 // the k rounds takes the wave maximum of the lanes' best remaining keys; the
-// winner is wave-uniform and its owner lane retires it.
+// winner is wave-uniform and its owner lane retires it.  The maximum is taken
+// on the 32-bit logit code first; when one lane holds that code (equal logits
+// in several lanes are rare) its key is the winner, otherwise the largest low
+// word (complemented expert id) among those lanes decides.
 template <int MAXS>
 __device__ __forceinline__ void topk_wave(const float *__restrict__ lg, int E, int k, int renorm,
                                           int lane, int32_t *idx_out, float *gate_out, int *sidx)
@@ -192,7 +190,12 @@ __device__ __forceinline__ void topk_wave(const float *__restrict__ lg, int E, i
 #pragma unroll
         for (int s = 0; s < MAXS; ++s)
             b = umax64(b, key[s]);
-        const uint64_t w = wave_max_u64(b);
+        const uint32_t bh = (uint32_t)(b >> 32), bl = (uint32_t)b;
+        const uint32_t mh = wave_max_u32(bh);
+        const uint64_t tied = __ballot(bh == mh);
+        const uint32_t ml = __popcll(tied) == 1 ? (uint32_t)__builtin_amdgcn_readlane((int)bl, __ffsll((long long)tied) - 1)
+                                                 : wave_max_u32(bh == mh ? bl : 0u);
+        const uint64_t w = ((uint64_t)mh << 32) | ml;
         const int we = (int)~(uint32_t)w;
         const float wv = key_value(w);
         if ((we & 63) == lane) {
