@@ -327,6 +327,25 @@ def test_decode_mxfp4_small(T, E, k, I):
     assert MX_DECODE_TOL <= TOL["mxfp4"]
 
 
+@pytest.mark.parametrize("w", ["f32", "bf16", "mxfp4"])
+@pytest.mark.parametrize("T", [1, 5, 40, 70])
+def test_hidden_not_a_power_of_two(w, T):
+    """d 2816 (11 x 256) and I 768 (6 x 128), 24 experts, top-3: the router's
+    last sweep over d covers part of the block, the GEMV row segments are 352
+    (gate/up) and 192 (down) elements long, and on the grouped-GEMM path (bf16
+    and MXFP4 at 70 tokens) the gate/up k-loop runs 44 k-tiles (not a multiple
+    of its three-stage unroll) over 6 column tiles and the down GEMM 11 column
+    tiles.  fp32 weights stay on the GEMV path at every T."""
+    cfg = cfg_small(hidden=2816, inter=768, experts=24, top_k=3, w_dtype=w, a_dtype="bf16", cid=170)
+    path = ecf.ECF_PATH_DECODE if (T <= 64 or w == "f32") else ecf.ECF_PATH_PREFILL
+    tol = TOL["f32"] if w == "f32" else (MX_DECODE_TOL if (w == "mxfp4" and path == ecf.ECF_PATH_DECODE) else TOL[w])
+    say(f"case: d 2816 I 768 w={w} T={T}")
+    c = Case(cfg, T)
+    res = c.run()
+    assert res["stats"]["path"] == path
+    compare(res, c.oracle(), tol, f"d 2816 w={w} T={T}")
+
+
 @pytest.mark.parametrize("T", [1, 16, 64])
 def test_decode_mxfp4_full_size(T):
     """The decode layer shape (d 4096, 256 experts, I 1024, top-6) with MXFP4 experts."""
