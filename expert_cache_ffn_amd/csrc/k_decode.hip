@@ -15,6 +15,8 @@
 // run the experts that are resident (FreeToken paper explainer, section
 // "Design: two-tier expert memory"; news.ainew.jp article on FreeToken, the
 // paragraph on the q* co-scheduling policy).
+#include <type_traits>
+
 #include "device_common.h"
 #include "ecf_internal.h"
 
@@ -75,13 +77,23 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
                                            false);
 }
 
+// The loops below take the number of staged rows either at run time (NTC = 0:
+// nt) or as a template argument (NTC = 1..kDecodeNT), and FULL = true when the
+// row segment is a whole number of load batches (no piece can pass its end):
+// with both fixed the unrolled loops carry no per-piece branches.  The MXFP4
+// gate/up GEMV runs that way (one token, I 1024: 12.3 -> 9.8 us); the other
+// GEMVs keep the run-time form, which the extra registers of the fixed one
+// made slower (bf16 down 100.7 -> 102.1 us, MXFP4 down 39.1 -> 40.5 us at 16
+// tokens; bf16 gate/up unchanged).
+
 // part[q][i] += w-pair i . x-pair i for the 4 bf16 pairs at element c (c % 8 == 0).
+template <int NTC>
 __device__ __forceinline__ void dot2_rows(const uint32_t (&w)[4], const uint16_t *__restrict__ xh, int ldp, int c,
                                           int nt, float (&part)[kDecodeNT][4])
 {
 #pragma unroll
     for (int q = 0; q < kDecodeNT; ++q) {
-        if (q < nt) {
+        if (q < (NTC ? NTC : nt)) {
             const uint4 xv = *reinterpret_cast<const uint4 *>(xh + q * ldp + xpadh(c));
             part[q][0] = dot2(w[0], xv.x, part[q][0]);
             part[q][1] = dot2(w[1], xv.y, part[q][1]);
@@ -92,13 +104,13 @@ __device__ __forceinline__ void dot2_rows(const uint32_t (&w)[4], const uint16_t
 }
 
 // part[q][i % 4] += w[i] * xs[q][c + i] over the nt staged rows.
-template <int N>
+template <int N, int NTC>
 __device__ __forceinline__ void fma_rows(const float (&w)[N], const float *__restrict__ xs, int ld, int c, int nt,
                                          float (&part)[kDecodeNT][4])
 {
 #pragma unroll
     for (int q = 0; q < kDecodeNT; ++q) {
-        if (q < nt) {
+        if (q < (NTC ? NTC : nt)) {
             const float *xp = xs + q * xpad_len(ld);
 #pragma unroll
             for (int i = 0; i < N; i += 4) {
@@ -131,13 +143,14 @@ struct RowRegs {
     uint4 wv[UNR];
     uint32_t sb[UNR];
 
+    template <bool FULL>
     __device__ __forceinline__ void load(const void *__restrict__ wrow, const uint8_t *__restrict__ srow, int c0,
                                          int kend)
     {
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
             const int c = c0 + u * 8 * V;
-            if (c < kend) {
+            if (FULL || c < kend) {
                 const size_t byte = WF == WF_MX ? (size_t)c / 2 : (size_t)c * (WF == WF_BF16 ? 2 : 4);
                 wv[u] = ld_nt16((const char *)wrow + byte);
                 if (WF == WF_MX)
@@ -146,13 +159,14 @@ struct RowRegs {
         }
     }
 
+    template <int NTC, bool FULL>
     __device__ __forceinline__ void apply(const float *__restrict__ xs, int ld, int c0, int kend, int nt,
                                           float (&part)[kDecodeNT][4]) const
     {
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
             const int c = c0 + u * 8 * V;
-            if (c >= kend)
+            if (!FULL && c >= kend)
                 break;
             const uint32_t p[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
             if (WF == WF_MX) {
@@ -164,7 +178,7 @@ struct RowRegs {
                     const f32x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p[i], sc, 2);
                     const f32x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p[i], sc, 3);
                     const float wf[8] = {v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
-                    fma_rows(wf, xs, ld, c + 8 * i, nt, part);
+                    fma_rows<8, NTC>(wf, xs, ld, c + 8 * i, nt, part);
                 }
             } else if (WF == WF_BF16) {
                 float wf[8];
@@ -173,26 +187,27 @@ struct RowRegs {
                     wf[2 * i] = bf_lo(p[i]);
                     wf[2 * i + 1] = bf_hi(p[i]);
                 }
-                fma_rows(wf, xs, ld, c, nt, part);
+                fma_rows<8, NTC>(wf, xs, ld, c, nt, part);
             } else {
                 float wf[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     wf[i] = __uint_as_float(p[i]);
-                fma_rows(wf, xs, ld, c, nt, part);
+                fma_rows<4, NTC>(wf, xs, ld, c, nt, part);
             }
         }
     }
 
     // Same sums against bf16-staged activations with bf16-pair dot products
     // (bf16 or MXFP4 weights; MXFP4 expands to bf16 pairs, exactly).
+    template <int NTC, bool FULL>
     __device__ __forceinline__ void apply2(const uint16_t *__restrict__ xh, int ldp, int c0, int kend, int nt,
                                            float (&part)[kDecodeNT][4]) const
     {
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
             const int c = c0 + u * 8 * V;
-            if (c >= kend)
+            if (!FULL && c >= kend)
                 break;
             const uint32_t p[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
             if (WF == WF_MX) {
@@ -204,10 +219,10 @@ struct RowRegs {
                         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(p[i], sc, 1)),
                         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(p[i], sc, 2)),
                         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(p[i], sc, 3))};
-                    dot2_rows(w, xh, ldp, c + 8 * i, nt, part);
+                    dot2_rows<NTC>(w, xh, ldp, c + 8 * i, nt, part);
                 }
             } else {
-                dot2_rows(p, xh, ldp, c, nt, part);
+                dot2_rows<NTC>(p, xh, ldp, c, nt, part);
             }
         }
     }
@@ -217,7 +232,7 @@ struct RowRegs {
 // the segment streams through registers one batch of UNR loads at a time.
 // Each row keeps 4 independent partial sums (element i of every 4 goes to
 // sum i), so the FMA chains are a quarter as long.
-template <int WF>
+template <int WF, int NTC, bool FULL>
 __device__ __forceinline__ void row_dots(const void *__restrict__ wrow, const uint8_t *__restrict__ srow,
                                          const float *__restrict__ xs, int ld, int kbeg, int kend, int sub, int nt,
                                          float acc[kDecodeNT])
@@ -225,8 +240,8 @@ __device__ __forceinline__ void row_dots(const void *__restrict__ wrow, const ui
     RowRegs<WF> rr;
     float part[kDecodeNT][4] = {};
     for (int c = kbeg + sub * RowRegs<WF>::V; c < kend; c += RowRegs<WF>::SPAN) {
-        rr.load(wrow, srow, c, kend);
-        rr.apply(xs, ld, c, kend, nt, part);
+        rr.template load<FULL>(wrow, srow, c, kend);
+        rr.template apply<NTC, FULL>(xs, ld, c, kend, nt, part);
     }
 #pragma unroll
     for (int q = 0; q < kDecodeNT; ++q)
@@ -264,7 +279,7 @@ __device__ __forceinline__ void piece_f32(const RowRegs<WF, UNR> &rr, int u, int
 }
 
 // apply() of RPG rows at once against fp32-staged activations.
-template <int WF, int RPG, int UNR>
+template <int WF, int RPG, int UNR, int NTC, bool FULL>
 __device__ __forceinline__ void apply_rows(const RowRegs<WF, UNR> (&rr)[RPG], const float *__restrict__ xs, int ld,
                                            int c0, int kend, int nt, float (&part)[RPG][kDecodeNT][4])
 {
@@ -274,7 +289,7 @@ __device__ __forceinline__ void apply_rows(const RowRegs<WF, UNR> (&rr)[RPG], co
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
         const int c = c0 + u * 8 * V;
-        if (c >= kend)
+        if (!FULL && c >= kend)
             break;
 #pragma unroll
         for (int pc = 0; pc < NP; ++pc) {
@@ -284,7 +299,7 @@ __device__ __forceinline__ void apply_rows(const RowRegs<WF, UNR> (&rr)[RPG], co
                 piece_f32(rr[r], u, pc, wf[r]);
 #pragma unroll
             for (int q = 0; q < kDecodeNT; ++q) {
-                if (q < nt) {
+                if (q < (NTC ? NTC : nt)) {
                     const float *xp = xs + q * xpad_len(ld);
 #pragma unroll
                     for (int i = 0; i < NE; i += 4) {
@@ -304,7 +319,7 @@ __device__ __forceinline__ void apply_rows(const RowRegs<WF, UNR> (&rr)[RPG], co
 }
 
 // apply2() of RPG rows at once against bf16-staged activations.
-template <int WF, int RPG, int UNR>
+template <int WF, int RPG, int UNR, int NTC, bool FULL>
 __device__ __forceinline__ void apply2_rows(const RowRegs<WF, UNR> (&rr)[RPG], const uint16_t *__restrict__ xh,
                                             int ldp, int c0, int kend, int nt, float (&part)[RPG][kDecodeNT][4])
 {
@@ -313,7 +328,7 @@ __device__ __forceinline__ void apply2_rows(const RowRegs<WF, UNR> (&rr)[RPG], c
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
         const int c = c0 + u * 8 * V;
-        if (c >= kend)
+        if (!FULL && c >= kend)
             break;
 #pragma unroll
         for (int pc = 0; pc < NP; ++pc) {
@@ -333,7 +348,7 @@ __device__ __forceinline__ void apply2_rows(const RowRegs<WF, UNR> (&rr)[RPG], c
             }
 #pragma unroll
             for (int q = 0; q < kDecodeNT; ++q) {
-                if (q < nt) {
+                if (q < (NTC ? NTC : nt)) {
                     const uint4 xv = *reinterpret_cast<const uint4 *>(xh + q * ldp + xpadh(c + 8 * pc));
 #pragma unroll
                     for (int r = 0; r < RPG; ++r) {
@@ -352,7 +367,7 @@ __device__ __forceinline__ void apply2_rows(const RowRegs<WF, UNR> (&rr)[RPG], c
 // before any of them is used (RPG times the loads in flight), then the rows
 // meet the staged activations together, each piece read from LDS once for all
 // RPG rows (MXFP4 down at 16 tokens 50 -> 41 us, its LDS reads a quarter).
-template <int WF, int RPG>
+template <int WF, int RPG, int NTC, bool FULL>
 __device__ __forceinline__ void row_dots_multi(const char *const (&wrow)[RPG], const uint8_t *const (&srow)[RPG],
                                                const float *__restrict__ xs, int ld, int kbeg, int kend, int sub,
                                                int nt, float (&acc)[RPG][kDecodeNT])
@@ -364,8 +379,8 @@ __device__ __forceinline__ void row_dots_multi(const char *const (&wrow)[RPG], c
     for (int c = kbeg + sub * Regs::V; c < kend; c += Regs::SPAN) {
 #pragma unroll
         for (int r = 0; r < RPG; ++r)
-            rr[r].load(wrow[r], srow[r], c, kend);
-        apply_rows<WF, RPG>(rr, xs, ld, c, kend, nt, part);
+            rr[r].template load<FULL>(wrow[r], srow[r], c, kend);
+        apply_rows<WF, RPG, Regs::UNR, NTC, FULL>(rr, xs, ld, c, kend, nt, part);
     }
 #pragma unroll
     for (int r = 0; r < RPG; ++r)
@@ -375,7 +390,7 @@ __device__ __forceinline__ void row_dots_multi(const char *const (&wrow)[RPG], c
 }
 
 // row_dots2 over RPG rows at once (as row_dots_multi).
-template <int WF, int RPG>
+template <int WF, int RPG, int NTC, bool FULL>
 __device__ __forceinline__ void row_dots2_multi(const char *const (&wrow)[RPG], const uint8_t *const (&srow)[RPG],
                                                 const uint16_t *__restrict__ xh, int ldp, int kbeg, int kend,
                                                 int sub, int nt, float (&acc)[RPG][kDecodeNT])
@@ -386,8 +401,8 @@ __device__ __forceinline__ void row_dots2_multi(const char *const (&wrow)[RPG], 
     for (int c = kbeg + sub * Regs::V; c < kend; c += Regs::SPAN) {
 #pragma unroll
         for (int r = 0; r < RPG; ++r)
-            rr[r].load(wrow[r], srow[r], c, kend);
-        apply2_rows<WF, RPG>(rr, xh, ldp, c, kend, nt, part);
+            rr[r].template load<FULL>(wrow[r], srow[r], c, kend);
+        apply2_rows<WF, RPG, Regs::UNR, NTC, FULL>(rr, xh, ldp, c, kend, nt, part);
     }
 #pragma unroll
     for (int r = 0; r < RPG; ++r)
@@ -397,7 +412,7 @@ __device__ __forceinline__ void row_dots2_multi(const char *const (&wrow)[RPG], 
 }
 
 // row_dots against bf16-staged activations (bf16 or MXFP4 weights).
-template <int WF>
+template <int WF, int NTC, bool FULL>
 __device__ __forceinline__ void row_dots2(const void *__restrict__ wrow, const uint8_t *__restrict__ srow,
                                           const uint16_t *__restrict__ xh, int ldp, int kbeg, int kend, int sub,
                                           int nt, float acc[kDecodeNT])
@@ -405,12 +420,30 @@ __device__ __forceinline__ void row_dots2(const void *__restrict__ wrow, const u
     RowRegs<WF> rr;
     float part[kDecodeNT][4] = {};
     for (int c = kbeg + sub * RowRegs<WF>::V; c < kend; c += RowRegs<WF>::SPAN) {
-        rr.load(wrow, srow, c, kend);
-        rr.apply2(xh, ldp, c, kend, nt, part);
+        rr.template load<FULL>(wrow, srow, c, kend);
+        rr.template apply2<NTC, FULL>(xh, ldp, c, kend, nt, part);
     }
 #pragma unroll
     for (int q = 0; q < kDecodeNT; ++q)
         acc[q] += (part[q][0] + part[q][1]) + (part[q][2] + part[q][3]);
+}
+
+// f(integral_constant<int, nt>, bool_constant<full>) for nt in 1..kDecodeNT
+template <typename F>
+__device__ __forceinline__ void dispatch_rows_full(int nt, bool full, F &f)
+{
+    static_assert(kDecodeNT == 2, "one instance per row count");
+    if (nt >= 2) {
+        if (full)
+            f(std::integral_constant<int, 2>{}, std::true_type{});
+        else
+            f(std::integral_constant<int, 2>{}, std::false_type{});
+    } else {
+        if (full)
+            f(std::integral_constant<int, 1>{}, std::true_type{});
+        else
+            f(std::integral_constant<int, 1>{}, std::false_type{});
+    }
 }
 
 // gate/up + SwiGLU.  Block = IB intermediate rows (gate and up) of one active
@@ -431,6 +464,8 @@ __global__ __launch_bounds__(256) void k_decode_gateup(
     constexpr int RPG = 2 * IB * KP / 32, OG = 2 * IB / RPG;
     constexpr bool DOT2 = ABF && WF != WF_F32;
     static_assert(RPG == 1 || DOT2, "two rows per group only on the bf16-pair path");
+    // elements a group covers per batch of loads (as row_dots2_multi / row_dots2 / row_dots take them)
+    constexpr int kSpan = RPG > 1 ? RowRegs<WF, (kRowUnr<WF> / RPG > 0 ? kRowUnr<WF> / RPG : 1)>::SPAN : RowRegs<WF>::SPAN;
     // [min(kDecodeNT, T)][xpadh_len(d)] bf16 (DOT2) or [..][xpad_len(d)] fp32; an expert has at most T rows
     extern __shared__ float xs[];
     uint16_t *xh = reinterpret_cast<uint16_t *>(xs);
@@ -474,12 +509,20 @@ __global__ __launch_bounds__(256) void k_decode_gateup(
         __syncthreads();
         {
             float acc[RPG][kDecodeNT] = {};
-            if (RPG > 1)
-                row_dots2_multi<WF, RPG>(wrow, srow, xh, xpadh_len(d), kbeg, kend, sub, nt, acc);
-            else if (DOT2)
-                row_dots2<WF>(wrow[0], srow[0], xh, xpadh_len(d), kbeg, kend, sub, nt, acc[0]);
+            auto dots = [&](auto ntc, auto fullc) __attribute__((always_inline)) {
+                constexpr int NTC = decltype(ntc)::value;
+                constexpr bool FULL = decltype(fullc)::value;
+                if (RPG > 1)
+                    row_dots2_multi<WF, RPG, NTC, FULL>(wrow, srow, xh, xpadh_len(d), kbeg, kend, sub, nt, acc);
+                else if (DOT2)
+                    row_dots2<WF, NTC, FULL>(wrow[0], srow[0], xh, xpadh_len(d), kbeg, kend, sub, nt, acc[0]);
+                else
+                    row_dots<WF, NTC, FULL>(wrow[0], srow[0], xs, d, kbeg, kend, sub, nt, acc[0]);
+            };
+            if (WF == WF_MX)
+                dispatch_rows_full(nt, Lk % kSpan == 0, dots);
             else
-                row_dots<WF>(wrow[0], srow[0], xs, d, kbeg, kend, sub, nt, acc[0]);
+                dots(std::integral_constant<int, 0>{}, std::false_type{});
 #pragma unroll
             for (int r = 0; r < RPG; ++r)
 #pragma unroll
@@ -555,10 +598,15 @@ __global__ __launch_bounds__(256) void k_decode_down(
         __syncthreads();
         {
             float acc[RPG][kDecodeNT] = {};
-            if (RPG == 1)
-                row_dots<WF>(wrow[0], srow[0], hs, I, kbeg, kend, sub, nt, acc[0]);
-            else
-                row_dots_multi<WF, RPG>(wrow, srow, hs, I, kbeg, kend, sub, nt, acc);
+            auto dots = [&](auto ntc, auto fullc) __attribute__((always_inline)) {
+                constexpr int NTC = decltype(ntc)::value;
+                constexpr bool FULL = decltype(fullc)::value;
+                if (RPG == 1)
+                    row_dots<WF, NTC, FULL>(wrow[0], srow[0], hs, I, kbeg, kend, sub, nt, acc[0]);
+                else
+                    row_dots_multi<WF, RPG, NTC, FULL>(wrow, srow, hs, I, kbeg, kend, sub, nt, acc);
+            };
+            dots(std::integral_constant<int, 0>{}, std::false_type{});
 #pragma unroll
             for (int r = 0; r < RPG; ++r)
 #pragma unroll
