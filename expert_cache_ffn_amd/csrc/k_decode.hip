@@ -81,20 +81,27 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
 // nt) or as a template argument (NTC = 1..kDecodeNT), and FULL = true when the
 // row segment is a whole number of load batches (no piece can pass its end):
 // with both fixed the unrolled loops carry no per-piece branches.  The MXFP4
-// gate/up GEMV runs that way (one token, I 1024: 12.3 -> 9.8 us); the other
+// gate/up GEMV runs that way (one token, I 1024: 12.3 -> 10.2 us); the other
 // GEMVs keep the run-time form, which the extra registers of the fixed one
 // made slower (bf16 down 100.7 -> 102.1 us, MXFP4 down 39.1 -> 40.5 us at 16
 // tokens; bf16 gate/up unchanged).
 
-// part[q][i] += w-pair i . x-pair i for the 4 bf16 pairs at element c (c % 8 == 0).
+// Activation offsets below are already padded: cp = xpad(c) or xpadh(c) of the
+// piece's first element c.  A piece (8 elements from c % 8 == 0, or 4) never
+// crosses a pad, so element c + i sits at cp + i.  For MXFP4 each batch starts
+// at a multiple of 32 (a 16-byte load holds 32 elements, and segments start at
+// multiples of 32), and xpad(c0 + off) = xpad(c0) + xpad(off) for c0 % 32 == 0:
+// the offsets are then one base per batch plus constants.
+
+// part[q][i] += w-pair i . x-pair i for the 4 bf16 pairs at padded offset cp.
 template <int NTC>
-__device__ __forceinline__ void dot2_rows(const uint32_t (&w)[4], const uint16_t *__restrict__ xh, int ldp, int c,
+__device__ __forceinline__ void dot2_rows(const uint32_t (&w)[4], const uint16_t *__restrict__ xh, int ldp, int cp,
                                           int nt, float (&part)[kDecodeNT][4])
 {
 #pragma unroll
     for (int q = 0; q < kDecodeNT; ++q) {
         if (q < (NTC ? NTC : nt)) {
-            const uint4 xv = *reinterpret_cast<const uint4 *>(xh + q * ldp + xpadh(c));
+            const uint4 xv = *reinterpret_cast<const uint4 *>(xh + q * ldp + cp);
             part[q][0] = dot2(w[0], xv.x, part[q][0]);
             part[q][1] = dot2(w[1], xv.y, part[q][1]);
             part[q][2] = dot2(w[2], xv.z, part[q][2]);
@@ -103,9 +110,9 @@ __device__ __forceinline__ void dot2_rows(const uint32_t (&w)[4], const uint16_t
     }
 }
 
-// part[q][i % 4] += w[i] * xs[q][c + i] over the nt staged rows.
+// part[q][i % 4] += w[i] * xs[q][c + i] over the nt staged rows (cp = xpad(c)).
 template <int N, int NTC>
-__device__ __forceinline__ void fma_rows(const float (&w)[N], const float *__restrict__ xs, int ld, int c, int nt,
+__device__ __forceinline__ void fma_rows(const float (&w)[N], const float *__restrict__ xs, int ld, int cp, int nt,
                                          float (&part)[kDecodeNT][4])
 {
 #pragma unroll
@@ -114,7 +121,7 @@ __device__ __forceinline__ void fma_rows(const float (&w)[N], const float *__res
             const float *xp = xs + q * xpad_len(ld);
 #pragma unroll
             for (int i = 0; i < N; i += 4) {
-                const float4 xv = *reinterpret_cast<const float4 *>(xp + xpad(c + i));
+                const float4 xv = *reinterpret_cast<const float4 *>(xp + cp + i);
                 part[q][0] = fmaf(w[i], xv.x, part[q][0]);
                 part[q][1] = fmaf(w[i + 1], xv.y, part[q][1]);
                 part[q][2] = fmaf(w[i + 2], xv.z, part[q][2]);
@@ -163,6 +170,7 @@ struct RowRegs {
     __device__ __forceinline__ void apply(const float *__restrict__ xs, int ld, int c0, int kend, int nt,
                                           float (&part)[kDecodeNT][4]) const
     {
+        const int xb = xpad(c0);  // MXFP4: c0 % 32 == 0
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
             const int c = c0 + u * 8 * V;
@@ -178,7 +186,7 @@ struct RowRegs {
                     const f32x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p[i], sc, 2);
                     const f32x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p[i], sc, 3);
                     const float wf[8] = {v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
-                    fma_rows<8, NTC>(wf, xs, ld, c + 8 * i, nt, part);
+                    fma_rows<8, NTC>(wf, xs, ld, xb + xpad(u * 8 * V + 8 * i), nt, part);
                 }
             } else if (WF == WF_BF16) {
                 float wf[8];
@@ -187,13 +195,13 @@ struct RowRegs {
                     wf[2 * i] = bf_lo(p[i]);
                     wf[2 * i + 1] = bf_hi(p[i]);
                 }
-                fma_rows<8, NTC>(wf, xs, ld, c, nt, part);
+                fma_rows<8, NTC>(wf, xs, ld, xpad(c), nt, part);
             } else {
                 float wf[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     wf[i] = __uint_as_float(p[i]);
-                fma_rows<4, NTC>(wf, xs, ld, c, nt, part);
+                fma_rows<4, NTC>(wf, xs, ld, xpad(c), nt, part);
             }
         }
     }
@@ -204,6 +212,7 @@ struct RowRegs {
     __device__ __forceinline__ void apply2(const uint16_t *__restrict__ xh, int ldp, int c0, int kend, int nt,
                                            float (&part)[kDecodeNT][4]) const
     {
+        const int xb = xpadh(c0);  // MXFP4: c0 % 32 == 0
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
             const int c = c0 + u * 8 * V;
@@ -219,10 +228,10 @@ struct RowRegs {
                         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(p[i], sc, 1)),
                         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(p[i], sc, 2)),
                         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(p[i], sc, 3))};
-                    dot2_rows<NTC>(w, xh, ldp, c + 8 * i, nt, part);
+                    dot2_rows<NTC>(w, xh, ldp, xb + xpadh(u * 8 * V + 8 * i), nt, part);
                 }
             } else {
-                dot2_rows<NTC>(p, xh, ldp, c, nt, part);
+                dot2_rows<NTC>(p, xh, ldp, xpadh(c), nt, part);
             }
         }
     }
@@ -283,6 +292,7 @@ template <int WF, int RPG, int UNR, int NTC, bool FULL>
 __device__ __forceinline__ void apply_rows(const RowRegs<WF, UNR> (&rr)[RPG], const float *__restrict__ xs, int ld,
                                            int c0, int kend, int nt, float (&part)[RPG][kDecodeNT][4])
 {
+    const int xb = xpad(c0);  // MXFP4: c0 % 32 == 0
     constexpr int V = RowRegs<WF, UNR>::V;
     constexpr int NP = WF == WF_MX ? 4 : 1;                       // pieces per 16-B load
     constexpr int NE = WF == WF_MX ? 8 : (WF == WF_BF16 ? 8 : 4);  // weights per piece
@@ -303,7 +313,8 @@ __device__ __forceinline__ void apply_rows(const RowRegs<WF, UNR> (&rr)[RPG], co
                     const float *xp = xs + q * xpad_len(ld);
 #pragma unroll
                     for (int i = 0; i < NE; i += 4) {
-                        const float4 xv = *reinterpret_cast<const float4 *>(xp + xpad(c + 8 * pc + i));
+                        const float4 xv = *reinterpret_cast<const float4 *>(
+                            xp + (WF == WF_MX ? xb + xpad(u * 8 * V + 8 * pc) : xpad(c + 8 * pc)) + i);
 #pragma unroll
                         for (int r = 0; r < RPG; ++r) {
                             part[r][q][0] = fmaf(wf[r][i], xv.x, part[r][q][0]);
@@ -323,6 +334,7 @@ template <int WF, int RPG, int UNR, int NTC, bool FULL>
 __device__ __forceinline__ void apply2_rows(const RowRegs<WF, UNR> (&rr)[RPG], const uint16_t *__restrict__ xh,
                                             int ldp, int c0, int kend, int nt, float (&part)[RPG][kDecodeNT][4])
 {
+    const int xb = xpadh(c0);  // MXFP4: c0 % 32 == 0
     constexpr int V = RowRegs<WF, UNR>::V;
     constexpr int NP = WF == WF_MX ? 4 : 1;  // pieces of 8 elements per 16-B load
 #pragma unroll
@@ -349,7 +361,8 @@ __device__ __forceinline__ void apply2_rows(const RowRegs<WF, UNR> (&rr)[RPG], c
 #pragma unroll
             for (int q = 0; q < kDecodeNT; ++q) {
                 if (q < (NTC ? NTC : nt)) {
-                    const uint4 xv = *reinterpret_cast<const uint4 *>(xh + q * ldp + xpadh(c + 8 * pc));
+                    const uint4 xv = *reinterpret_cast<const uint4 *>(
+                        xh + q * ldp + (WF == WF_MX ? xb + xpadh(u * 8 * V + 8 * pc) : xpadh(c + 8 * pc)));
 #pragma unroll
                     for (int r = 0; r < RPG; ++r) {
                         part[r][q][0] = dot2(w[r][0], xv.x, part[r][q][0]);
@@ -451,8 +464,10 @@ __device__ __forceinline__ void dispatch_rows_full(int nt, bool full, F &f)
 // bf16 activations with bf16 or MXFP4 weights stay bf16 in LDS and meet the
 // weights in bf16-pair dot products (half the LDS reads and FMA instructions of
 // the fp32 form; every product is exact either way).
+// The 16-row MXFP4 form asks for four waves per SIMD (at most 128 registers):
+// left free it took 131 and ran three (16 tokens: 69.9 against 65.4 us).
 template <int WF, bool ABF, int IB, int KP>
-__global__ __launch_bounds__(256) void k_decode_gateup(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WF == WF_MX && IB >= 16 ? 4 : 1))) void k_decode_gateup(
     const uint64_t *__restrict__ ptrs, size_t off_gate, size_t off_up, size_t off_sgate, size_t off_sup,
     const int32_t *__restrict__ active, const int32_t *__restrict__ n_active,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm,
