@@ -283,12 +283,14 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_grouped_gemm(
                                                        : BNT / 2 + wn * (BNT / 2 / WN) + (cb - NCB / 2) * 32)
                                         : wn * (BNT / WN) + cb * 32);
     const int nk = K / BK;
-    // MODE 2 epilogue: wave w's 32 x kYst fp32 staging buffer, carved from the
-    // stage arrays (free by then) without crossing one
-    constexpr int kYst = 72;  // row stride: rows 4 apart land 32 banks apart
-    constexpr int kYslots = 32 * kYst / 4;  // 16-B slots per buffer
+    // Epilogue: wave w's staging buffer of 32 rows, carved from the stage arrays
+    // (free by then) without crossing one.  MODE 2: kYst fp32 per row (rows 4
+    // apart land 32 banks apart); MODE 1: kHst bf16 per row (80 B: rows 4
+    // apart land 16 banks apart, a half-wave writes 16 banks).
+    constexpr int kYst = 72, kHst = 40;
+    constexpr int kYslots = MODE == 2 ? 32 * kYst / 4 : 32 * kHst / 8;  // 16-B slots per buffer
     constexpr int nA = BM * 8 / kYslots, nB = BT / kYslots;  // buffers per A / B stage array
-    static_assert(MODE == 1 || 3 * nA + 3 * nB >= NW, "LDS for the staged Y");
+    static_assert(3 * nA + 3 * nB >= NW, "LDS for the staged output");
     auto ybuf_of_wave = [&](int wv) -> float * {
         constexpr int dA = nA > 0 ? nA : 1, dB = nB > 0 ? nB : 1;
         u32x4_t *p;
@@ -434,6 +436,32 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_grouped_gemm(
                         // Y is read once, by the combine: non-temporal stores
                         __builtin_nontemporal_store(
                             v, reinterpret_cast<f32x4v *>((float *)out + (size_t)(rb + m) * N + n0 + wn * (BNT / WN) + c4));
+                }
+                asm volatile("" ::: "memory");
+            }
+            return;
+        } else {
+            // H (bf16, after SwiGLU) goes out the same way: a wave's 32 x 32 block
+            // per row block, written to LDS 2 bytes per lane and read back by rows,
+            // 16 bytes per lane (2 stores per row block instead of 16; GEMM1
+            // +2.5% MXFP4, +1% bf16 in an interleaved A/B on one GPU)
+            __syncthreads();
+            static_assert(NCB == 2, "staged H: one gate and one up fragment per wave");
+            uint16_t *hb = reinterpret_cast<uint16_t *>(ybuf_of_wave(w));
+#pragma unroll
+            for (int ms = 0; ms < NMS; ++ms) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    hb[((j >> 2) * 8 + (l >> 5) * 4 + (j & 3)) * kHst + (l & 31)] =
+                        f_to_bf(silu_mul(acc[ms][0][j], acc[ms][1][j]));
+                asm volatile("" ::: "memory");
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int r = i * 16 + (l >> 2), c8 = (l & 3) * 8;
+                    const int m = wm * WROWS + ms * 32 + r;
+                    const uint4 v = *reinterpret_cast<const uint4 *>(hb + r * kHst + c8);
+                    if (m < mrows)
+                        *reinterpret_cast<uint4 *>((uint16_t *)out + (size_t)(rb + m) * N + n0 + wn * (BNT / 2 / WN) + c8) = v;
                 }
                 asm volatile("" ::: "memory");
             }
