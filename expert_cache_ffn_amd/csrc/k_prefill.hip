@@ -230,6 +230,8 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_grouped_gemm(
     // access (the range check takes the per-lane offset).  A resource of 2 GiB
     // or more cannot place such an offset; its pad rows re-read the last row.
     const bool a_oob = abytes < 0x80000000ull;
+    // both resources under 2 GiB: an offset of 2^31 reads nothing from either
+    const bool nil_ok = a_oob && blob_bytes < 0x80000000u;
     // load q of wave w fills tile rows 8 (q * NW + w) .. +7, lane l the slot of
     // row (tid >> 3) + (NTH / 8) q at position l & 7: the chunk swz puts there
     auto achunk = [](int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); };
@@ -317,7 +319,8 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_grouped_gemm(
                     acc[a][b][j] = 0.f;
         // MXFP4 scale words travel through registers two k-tiles ahead and are
         // widened into Scf for the next k-tile at the end of each k-tile.
-        auto sload = [&](int kt) -> uint32_t {
+        auto sload = [&](int kt, bool real) -> uint32_t {
+            (void)real;  // MXFP4 reloads the last k-tile's scales too (see dma_tile)
             return MX ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rbs, p.s, kt * 2, 0) : 0u;
         };
         auto sput = [&](uint32_t sc, float *dst) __attribute__((always_inline)) {
@@ -336,30 +339,37 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_grouped_gemm(
         // of a row; 800 -> 756 us for the 4096-token layer).  MXFP4 k-tiles take
         // 32 B of a line whose rest the next three k-tiles use, and the bf16 down
         // GEMM got slower with them: default policy there.
-        auto dma_tile = [&](u32x4_t *Ad, u32x4_t *Bd, int kt) __attribute__((always_inline)) {
+        // real = false: a k-tile past the end, loaded only so that every k-tile
+        // issues the same loads.  bf16: with resources under 2 GiB its offsets
+        // lie past them, so the loads read nothing (zeros into a stage nobody
+        // reads; bf16 GEMM1 +1.6% in an interleaved A/B).  MXFP4 reloads the last
+        // k-tile (reading nothing was 1.4% slower there).
+        auto dma_tile = [&](u32x4_t *Ad, u32x4_t *Bd, int kt, bool real) __attribute__((always_inline)) {
             const int col = kt * BK;
+            const bool nil = !MX && !real && nil_ok;
 #pragma unroll
             for (int q = 0; q < P::NAL; ++q)
-                lds_load16<0>(ra, Ad + q * NTH + 64 * w, p.a[q], col * 2);
+                lds_load16<0>(ra, Ad + q * NTH + 64 * w, nil ? 0x80000000u : p.a[q], col * 2);
 #pragma unroll
             for (int q = 0; q < P::NBL; ++q)
-                lds_load16<(!MX && MODE == 1) ? 2 : 0>(rbs, Bd + q * NTH + 64 * w, p.b[q], MX ? col / 2 : col * 2);
+                lds_load16<(!MX && MODE == 1) ? 2 : 0>(rbs, Bd + q * NTH + 64 * w, nil ? 0x80000000u : p.b[q],
+                                                       MX ? col / 2 : col * 2);
         };
-        dma_tile(A0, B0, 0);
-        const uint32_t sc0 = sload(0);
-        dma_tile(A1, B1, min(1, nk - 1));
-        uint32_t sc_next = sload(min(1, nk - 1));
+        dma_tile(A0, B0, 0, true);
+        const uint32_t sc0 = sload(0, true);
+        dma_tile(A1, B1, min(1, nk - 1), nk > 1);
+        uint32_t sc_next = sload(min(1, nk - 1), nk > 1);
         sput(sc0, Scf[0]);
         stage_barrier<NLD>();
         // One k-tile: the loads of k-tile kt+2 go out first (into the stage
         // k-tile kt-1 used), then the MFMAs of k-tile kt, then the wait for
-        // k-tile kt+1.  Past the end the last k-tile is loaded again into a stage
-        // nobody reads, so every k-tile issues the same NLD loads.
+        // k-tile kt+1.  Past the end a k-tile's loads go to a stage nobody reads
+        // (reading nothing, see dma_tile), so every k-tile issues the same NLD loads.
         auto body = [&](int kt, const u32x4_t *Ac, const u32x4_t *Bc, u32x4_t *An, u32x4_t *Bn)
                         __attribute__((always_inline)) {
             const int cur = kt & 1;
-            dma_tile(An, Bn, min(kt + 2, nk - 1));
-            const uint32_t sc_new = sload(min(kt + 2, nk - 1));
+            dma_tile(An, Bn, min(kt + 2, nk - 1), kt + 2 < nk);
+            const uint32_t sc_new = sload(min(kt + 2, nk - 1), kt + 2 < nk);
             // issue them here, two k-tiles ahead of their use (the scheduler
             // would otherwise sink them below the MFMAs)
             asm volatile("" ::: "memory");
