@@ -15,7 +15,11 @@
 namespace ecf {
 
 // Fixed pool of worker threads; parallel_for runs fn(0..n-1) on the workers
-// and the calling thread and returns when every index is done.
+// and the calling thread and returns when every index is done.  Idle workers
+// spin on the call counter for about 50 us before they sleep on the condition
+// variable, so back-to-back calls (an expert-cache layer-step makes three, a
+// few microseconds apart) start without a thread wake-up; the caller spins for
+// the last tasks to end.
 class HostPool {
 public:
     explicit HostPool(int n_threads);
@@ -29,15 +33,18 @@ public:
 private:
     void worker();
     void run_tasks(const std::function<void(int)> &fn, int total);
-    std::exception_ptr err_;
+    std::exception_ptr err_;  // under mu_
     std::vector<std::thread> th_;
     std::mutex mu_;
-    std::condition_variable cv_, done_cv_;
-    const std::function<void(int)> *fn_ = nullptr;
-    std::atomic<int> next_{0};
-    int total_ = 0, busy_ = 0;
-    uint64_t epoch_ = 0;
-    bool stop_ = false;
+    std::condition_variable cv_;
+    // Published before epoch_ is raised (release) and read after it is seen
+    // (acquire): the call's function and size.
+    std::atomic<const std::function<void(int)> *> fn_{nullptr};
+    std::atomic<int> total_{0};
+    std::atomic<int> next_{0};     // next index to run
+    std::atomic<int> busy_{0};     // workers still in the current call
+    std::atomic<uint64_t> epoch_{0};  // raised (under mu_) once per call and at shutdown
+    std::atomic<bool> stop_{false};
 };
 
 struct HostExpertJob {

@@ -1,18 +1,24 @@
 // Host-side checks of libecf's CPU code under the compiler's sanitizers
 // (AddressSanitizer + UndefinedBehaviorSanitizer in one build, ThreadSanitizer
-// in another): the shared LRU cache and its elastic resize, the q* split, and
-// the host expert FFN on its thread pool, all through the C ABI.  No GPU is
-// touched: the GPU kernel launchers are replaced by stubs (stubs.cpp) that are
-// never called, and no call below reaches a HIP runtime function.
+// in another): the shared LRU cache and its elastic resize, the q* split and
+// the host expert FFN on its thread pool, all through the C ABI, and the thread
+// pool itself through its internal header.  No GPU is touched: the GPU kernel
+// launchers are replaced by stubs (stubs.cpp) that are never called, and no
+// call below reaches a HIP runtime function.
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <random>
 #include <set>
+#include <stdexcept>
+#include <thread>
 #include <vector>
 
 #include "ecf.h"
+#include "../../expert_cache_ffn_amd/csrc/host_ffn.h"
 
 static int g_fail = 0;
 #define CHECK(c)                                                                  \
@@ -180,8 +186,48 @@ static void check_host_experts(int w_dtype)
     CHECK(ecf_host_experts(&s, E, bp.data(), n_rows.data(), bad.data(), x.data(), T, y8.data(), 4) == ECF_EINVAL);
 }
 
+// The host thread pool on its own: thousands of back-to-back calls of every
+// size from 0 to 64 (the workers spin between them), pauses long enough for
+// them to fall asleep, and calls in which a task throws (rethrown once per
+// call, the pool usable afterwards).
+static void check_pool()
+{
+    for (int nt : {1, 3, 8}) {
+        ecf::HostPool pool(nt);
+        std::vector<std::atomic<int>> hit(64);
+        for (int it = 0; it < 3000; ++it) {
+            const int n = it % 65;
+            for (auto &h : hit)
+                h.store(0, std::memory_order_relaxed);
+            pool.parallel_for(n, [&](int i) { hit[i].fetch_add(1, std::memory_order_relaxed); });
+            bool ok = true;
+            for (int i = 0; i < 64; ++i)
+                ok = ok && hit[i].load(std::memory_order_relaxed) == (i < n ? 1 : 0);
+            CHECK(ok);
+            if (it % 1000 == 999)
+                std::this_thread::sleep_for(std::chrono::milliseconds(5));
+        }
+        int caught = 0;
+        for (int it = 0; it < 20; ++it) {
+            try {
+                pool.parallel_for(40, [&](int i) {
+                    if (i == 7 + it % 3)
+                        throw std::runtime_error("task");
+                });
+            } catch (const std::runtime_error &) {
+                ++caught;
+            }
+        }
+        CHECK(caught == 20);
+        std::atomic<int> sum{0};
+        pool.parallel_for(100, [&](int i) { sum.fetch_add(i, std::memory_order_relaxed); });
+        CHECK(sum.load() == 4950);
+    }
+}
+
 int main()
 {
+    check_pool();
     check_qstar();
     for (unsigned seed = 1; seed <= 3; ++seed)
         check_cache(seed);
