@@ -203,6 +203,7 @@ def bench_decode(torch, ecf, syn, Ts, steps, warmup, n_batches=64, use_graph=Tru
     S = ecf.ecf_expert_bytes(shape)
     # gate + up bytes of one expert: the two weight sections (+ their scales for MXFP4)
     gu_expert = 2 * (I * d * 2 if w_dtype == "bf16" else I * d // 2 + I * d // 32)
+    dn_expert = d * I * 2 if w_dtype == "bf16" else d * I // 2 + d * I // 32  # down weights (+ scales)
     pool = ExpertPool(shape, "cuda")
     # host_inputs: every input is generated on the host and copied, so the only
     # GPU kernels of the run are libecf's and the runtime's copies (a hardware
@@ -292,6 +293,7 @@ def bench_decode(torch, ecf, syn, Ts, steps, warmup, n_batches=64, use_graph=Tru
         U_avg = float(U[used].mean())
         R = T * k
         gu_bytes = U_avg * gu_expert + R * d * 2 + R * I * 4           # gate+up weights, x rows, h
+        dn_bytes = U_avg * dn_expert + R * I * 4 + R * d * 4           # down weights, h, Y
         layer_bytes = U_avg * S + E * d * 2 + T * d * 2 + T * d * 4    # weights, router, x, out
         kern = {n: {"launches": c, "avg_us": 1e3 * t / max(c, 1)} for n, (c, t) in prof.items()}
         gu_us = kern["decode_gateup"]["avg_us"]
@@ -302,7 +304,10 @@ def bench_decode(torch, ecf, syn, Ts, steps, warmup, n_batches=64, use_graph=Tru
             layer_bytes=layer_bytes, layer_GBps=layer_bytes / (ms / steps * 1e-3) / 1e9,
             layer_hbm_frac=layer_bytes / (ms / steps * 1e-3) / 1e9 / HBM_PEAK_GBS,
             gateup_bytes=gu_bytes, gateup_avg_us=gu_us, gateup_GBps=gu_bytes / (gu_us * 1e-6) / 1e9,
-            kernels=kern, graph=use_graph)
+            down_bytes=dn_bytes, kernels=kern, graph=use_graph)
+        if "decode_down" in kern:  # one token of MXFP4 runs down and combine as one kernel
+            dn_us = kern["decode_down"]["avg_us"]
+            results[T].update(down_avg_us=dn_us, down_GBps=dn_bytes / (dn_us * 1e-6) / 1e9)
         # the same bytes read by one plain streaming kernel: the floor for the
         # whole layer, which is a chain of dependent kernels
         # (not in the host-input mode used for hardware-counter passes: the floor
