@@ -791,10 +791,11 @@ def cached_oracle_check(torch, syn, ctx, rec, lgs_step):
     return r
 
 
-def bench_cached(torch, ecf, syn, ctx, policy="lru_qstar", bw=None, oracle_check=False):
+def bench_cached(torch, ecf, syn, ctx, policy="lru_qstar", bw=None, oracle_check=False, track_misses=False):
     """One policy on the shared cached-decode setup; returns throughput and traffic.
     oracle_check: afterwards one more step is recorded layer by layer and checked
-    against (and timed beside) the oracle."""
+    against (and timed beside) the oracle.  track_misses: also return each timed
+    step's (trace step, (misses, lookups)) over its layers."""
     L, E, T, S = ctx["L"], ctx["E"], ctx["T"], ctx["S"]
     steps, warmup, lgs, lay = ctx["steps"], ctx["warmup"], ctx["lgs"], ctx["layer"]
     n_logits = len(lgs)
@@ -817,11 +818,13 @@ def bench_cached(torch, ecf, syn, ctx, policy="lru_qstar", bw=None, oracle_check
         raise ValueError(policy)
     totals = dict(unique=0, hits=0, gpu_experts=0, misses=0, q=0, host=0, h2d=0, hostb=0, wait=0.0, hostms=0.0)
     qhist = {}
+    per_step = []
     res_f, act, xa = ctx["res_f"], ctx["act"], ctx["xa"]
 
     def one_step(s, record, layers_out=None):
         x = xa
         res_f.zero_()
+        sm = [0, 0]
         for l in range(L):
             a = lay.args(layer=l, router_logits=lgs[s % n_logits][l], cache=cache, b_p=b_p, b_h=b_h,
                          q_mode=q_mode, copy_stream=ctx["cstream"], residual=res_f, out_act=act)
@@ -845,6 +848,10 @@ def bench_cached(torch, ecf, syn, ctx, policy="lru_qstar", bw=None, oracle_check
                 totals["wait"] += st["ms_wait_route"]
                 totals["hostms"] += st["ms_host_ffn"]
                 qhist[st["q"]] = qhist.get(st["q"], 0) + 1
+                sm[0] += st["misses"]
+                sm[1] += st["n_unique"]
+        if record and track_misses:
+            per_step.append((s, tuple(sm)))
 
     torch.cuda.synchronize()
     st0 = ecf.ecf_cache_get_stats(cache)
@@ -879,10 +886,49 @@ def bench_cached(torch, ecf, syn, ctx, policy="lru_qstar", bw=None, oracle_check
                host_threads="default (min(16, hardware threads))")
     if oracle_res is not None:
         res["cpu_oracle"] = oracle_res
+    if track_misses:
+        res["per_step_misses"] = per_step
     log(f"cached {ctx['w_dtype']} [{policy}]: {res['ms_per_step']:.1f} ms/step ({L} layers), {res['tokens_per_s']:.1f} tok/s, "
         f"steady miss rate {100 * miss_steady:.1f}%, PCIe {res['pcie_GBps']:.1f} GB/s, "
         f"host {res['host_read_GBps']:.1f} GB/s, HBM (expert weights) {res['hbm_expert_GBps']:.1f} GB/s")
     return res
+
+
+DRIFT_POLICIES = ("lru_qstar", "lru_qstar_measured", "static_hot")
+
+
+def bench_drift(torch, ecf, syn, ctx, bw, args):
+    """The policy ablation at 16 tokens on a trace whose hot set moves: each
+    layer's Zipf(1.1) ranking is redrawn every args.drift_steps steps (a new
+    seeded permutation per phase).  The static subset is bound once from the
+    first phase's law, as a placement fixed at load or prefill time is; the
+    shared LRU follows the routing.  Besides the whole timed window, each
+    policy's miss rate is split into the first 8 steps after each phase change
+    and the rest."""
+    import dataclasses
+    saved = {n: ctx[n] for n in ("cfg", "steps", "warmup")}
+    ctx.update(cfg=dataclasses.replace(saved["cfg"], drift_steps=args.drift_steps), steps=args.drift_timed,
+               warmup=args.cached_warmup)
+    cached_tokens(torch, syn, ctx, 16)
+    out = {"drift_steps": args.drift_steps, "warmup": ctx["warmup"], "steps": ctx["steps"],
+           "phases_timed": sorted({syn.phase_of(ctx["cfg"], s)
+                                   for s in range(ctx["warmup"], ctx["warmup"] + ctx["steps"])})}
+    for p in DRIFT_POLICIES:
+        r = bench_cached(torch, ecf, syn, ctx, p, bw, track_misses=True)
+        r.pop("q_hist")
+        per = r.pop("per_step_misses")
+        fresh = [m for s, m in per if s % args.drift_steps < 8]
+        rest = [m for s, m in per if s % args.drift_steps >= 8]
+        frac = lambda v: sum(m for m, _ in v) / max(1, sum(n for _, n in v))
+        r["miss_rate_first8_after_change"] = frac(fresh)
+        r["miss_rate_rest_of_phase"] = frac(rest)
+        out[p] = r
+        log(f"drift [{p}]: miss rate {100 * r['miss_rate_steady']:.1f}% (first 8 steps of a phase "
+            f"{100 * r['miss_rate_first8_after_change']:.1f}%, rest {100 * r['miss_rate_rest_of_phase']:.1f}%), "
+            f"{r['tokens_per_s']:.1f} tok/s")
+    ctx.update(saved)
+    ctx.pop("lgs", None)
+    return out
 
 
 def bench_bandwidth(torch, ecf, ctx, seconds=2.0):
@@ -911,16 +957,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workloads",
                     default="hbm,decode,decode_fp4,prefill,prefill_fp4,vendor,prefetch,cached,bandwidth,policies,"
-                            "cached_fp4",
+                            "drift,cached_fp4",
                     help="any of hbm, decode, decode_fp4, prefill, prefill_fp4, vendor, prefetch, cached, bandwidth, "
-                         "policies, cached_fp4 (policies: the cached-decode policy ablation at equal capacity; *_fp4: "
-                         "the same layers with MXFP4 experts; vendor: torch.bmm on the prefill GEMM shapes)")
+                         "policies, drift, cached_fp4 (policies: the cached-decode policy ablation at equal capacity; "
+                         "drift: the same ablation on a trace whose popularity ranking moves; *_fp4: the same layers "
+                         "with MXFP4 experts; vendor: torch.bmm on the prefill GEMM shapes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--cached-steps", type=int, default=32, help="cached decode timed steps per policy and batch size")
     ap.add_argument("--cached-warmup", type=int, default=16, help="cached decode warm-up steps (the LRU fills)")
     ap.add_argument("--policies", default=",".join(POLICIES), help="policies the 'policies' workload compares")
     ap.add_argument("--cached-tokens", default="1,4,16", help="cached-decode batch sizes (cached, policies)")
+    ap.add_argument("--drift-steps", type=int, default=32,
+                    help="drift workload: steps per popularity phase (each layer's Zipf ranking redrawn)")
+    ap.add_argument("--drift-timed", type=int, default=80, help="drift workload: timed steps per policy")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run one plain 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--host-inputs", action="store_true",
@@ -990,13 +1040,13 @@ def main():
     if "prefetch" in wl:
         also["prefill_bf16_streamed_stack"] = bench_prefetch(torch, ecf, syn, "prefill")
         also["prefill_mxfp4_streamed_stack"] = bench_prefetch(torch, ecf, syn, "prefill_fp4")
-    if wl & {"cached", "bandwidth", "policies"}:
+    if wl & {"cached", "bandwidth", "policies", "drift"}:
         cw = args.cached_steps if args.cached_warmup is None else args.cached_warmup
         ctx = cached_setup(torch, ecf, syn, steps=args.cached_steps, warmup=cw)
         bw = None
-        if wl & {"bandwidth", "policies"}:
+        if wl & {"bandwidth", "policies", "drift"}:
             bw = also["bandwidth_profile"] = bench_bandwidth(torch, ecf, ctx)
-        for T in (int(t) for t in args.cached_tokens.split(",")):
+        for T in (int(t) for t in args.cached_tokens.split(",") if wl & {"cached", "policies"}):
             cached_tokens(torch, syn, ctx, T)
             if "cached" in wl:
                 also[f"cached_decode_43L_T{T}"] = bench_cached(
@@ -1008,6 +1058,8 @@ def main():
                 for r in pol.values():
                     r.pop("q_hist")
                 also[f"cached_policies_43L_T{T}"] = pol
+        if "drift" in wl:
+            also["cached_policies_43L_T16_drift"] = bench_drift(torch, ecf, syn, ctx, bw, args)
         del ctx
         torch.cuda.empty_cache()
     if "cached_fp4" in wl:

@@ -26,4 +26,5 @@ from .gen import (  # noqa: F401
     router_logits,
     zipf_gumbel_logits,
     popularity_rank,
+    phase_of,
 )

@@ -145,6 +145,11 @@ class Config:
     layers: int = 1
     temperature: float = 1.0
     zipf_s: float = 1.1
+    # "zipf" logits: 0 keeps one popularity law per layer for the whole trace;
+    # n > 0 draws a new ranking of each layer's experts every n steps (phase
+    # step // n), a trace whose hot set moves, as the working set of a served
+    # session does between turns
+    drift_steps: int = 0
 
 
 CONFIGS = {
@@ -193,13 +198,19 @@ def expert_weights(cfg: Config, layer: int, expert: int, device="cpu", dtype=Non
     return out
 
 
-def popularity_rank(cfg: Config, layer: int, device="cpu") -> torch.Tensor:
-    """Rank (1 = most popular) of each expert of `layer` in the Zipf recipe, fp64 [E]."""
+def popularity_rank(cfg: Config, layer: int, device="cpu", phase: int = 0) -> torch.Tensor:
+    """Rank (1 = most popular) of each expert of `layer` in the Zipf recipe, fp64 [E].
+    `phase` selects the ranking of a drifting trace (phase 0 is the stationary one)."""
     E = cfg.experts
-    u = uniform(key_of(cfg.cid, layer, T_PERM), E, device)
+    u = uniform(key_of(cfg.cid, layer, T_PERM, 0, phase), E, device)
     rank = torch.empty(E, dtype=torch.float64, device=device)
     rank[torch.argsort(u, stable=True)] = torch.arange(1, E + 1, dtype=torch.float64, device=device)
     return rank
+
+
+def phase_of(cfg: Config, step: int) -> int:
+    """Popularity phase of a step: 0 throughout unless cfg.drift_steps > 0."""
+    return step // cfg.drift_steps if cfg.drift_steps > 0 else 0
 
 
 def zipf_gumbel_logits(cfg: Config, layer: int, step: int, T: int, device="cpu"):
@@ -210,9 +221,10 @@ def zipf_gumbel_logits(cfg: Config, layer: int, step: int, T: int, device="cpu")
     expert) adds an independent Gumbel(0, 1) draw to log p, so the k largest
     logits are a sample of k experts without replacement with weights p
     (the Gumbel-top-k construction of Kool, van Hoof and Welling, ICML 2019).
+    With cfg.drift_steps = n > 0 the ranking is redrawn every n steps.
     """
     E = cfg.experts
-    rank = popularity_rank(cfg, layer, device)
+    rank = popularity_rank(cfg, layer, device, phase_of(cfg, step))
     logp = -cfg.zipf_s * torch.log(rank)
     logp = logp - torch.logsumexp(logp, 0)
     g = uniform(key_of(cfg.cid, layer, T_LOGITS, 0, step), T * E, device).view(T, E)

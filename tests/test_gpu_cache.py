@@ -451,17 +451,19 @@ def _hot_set(cfg, n_slots):
             for l in range(cfg.layers)]
 
 
-@pytest.mark.parametrize("policy", ["static_hot", "all_pcie"])
-def test_policy_ablation_small(policy):
+@pytest.mark.parametrize("policy,drift", [("static_hot", 0), ("all_pcie", 0), ("static_hot", 3), ("all_pcie", 3)])
+def test_policy_ablation_small(policy, drift):
     """The two comparison policies at equal capacity (37% of the pairs), through
     the C ABI: a static hot subset (the most popular pairs bound once with
     expert_cache_lookup / expert_cache_evict and filled, then every miss on the
     host, q = 0) and the shared LRU with every miss copied (q = m).  Each step's
     output matches the oracle and the all-resident layer, and its hit / miss /
     copy counts match a Python reference of the policy (a fixed set for the
-    static subset, the reference LRU for all-PCIe)."""
+    static subset, the reference LRU for all-PCIe).  drift > 0: each layer's
+    popularity ranking is redrawn every `drift` steps, while the static subset
+    stays the one bound from the first ranking."""
     E, L, T, k = 16, 3, 4, 4
-    cfg = syn.gen.Config(106, "pol", (T,), 512, E, 256, k, "bf16", "bf16", "zipf", layers=L)
+    cfg = syn.gen.Config(106, "pol", (T,), 512, E, 256, k, "bf16", "bf16", "zipf", layers=L, drift_steps=drift)
     d = cfg.hidden
     n_slots = int(0.37 * L * E)
     cs = CachedSetup(cfg, L, n_slots=n_slots)

@@ -323,3 +323,60 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=120)
     assert p.returncode == 2
     assert "one GPU" in p.stdout
+
+
+def test_drifting_zipf_phases():
+    """The drifting trace's popularity: phase 0 is the stationary ranking, a
+    phase keeps one ranking for drift_steps steps, and the next phase draws
+    another one (a permutation of the same ranks)."""
+    import dataclasses
+    base = syn.CONFIGS["cached"]
+    cfg = dataclasses.replace(base, drift_steps=4)
+    assert [syn.phase_of(cfg, s) for s in (0, 3, 4, 7, 8)] == [0, 0, 1, 1, 2]
+    assert [syn.phase_of(base, s) for s in (0, 5, 500)] == [0, 0, 0]
+    r0 = syn.popularity_rank(base, 3)
+    assert torch.equal(syn.popularity_rank(cfg, 3, phase=0), r0)
+    r1 = syn.popularity_rank(cfg, 3, phase=1)
+    assert not torch.equal(r1, r0)
+    assert torch.equal(torch.sort(r1).values, torch.arange(1, cfg.experts + 1, dtype=torch.float64))
+    assert torch.equal(syn.router_logits(cfg, 2, layer=3, step=2), syn.router_logits(base, 2, layer=3, step=2))
+    # step 5 lies in phase 1: its logits add the same Gumbel draws to the phase-1 law
+    g = syn.router_logits(base, 2, layer=3, step=5) - syn.router_logits(cfg, 2, layer=3, step=5)
+    assert not torch.allclose(g, torch.zeros_like(g))
+
+
+def test_lru_on_drifting_trace_against_reference():
+    """The C-ABI LRU on the drifting Zipf trace (rankings redrawn every 8 steps)
+    makes the reference LRU's decisions; on such a trace the LRU ends with fewer
+    misses than a subset fixed from the first phase's law at equal capacity."""
+    import dataclasses
+    cfg = dataclasses.replace(syn.CONFIGS["cached"], experts=64, layers=4, drift_steps=8)
+    L, E, k, T = cfg.layers, cfg.experts, cfg.top_k, 16
+    n_slots = int(0.37 * L * E)
+    per, extra = divmod(n_slots, L)
+    hot = [set(int(e) for e in (syn.popularity_rank(cfg, l) <= per + (1 if l < extra else 0)).nonzero().flatten())
+           for l in range(L)]
+    cache = ecf.ecf_cache_create(L, E, n_slots, n_slots, 4096, FAKE_SLOTS)
+    ref = oracle.LRURef(n_slots, E)
+    miss_lru = miss_static = 0
+    try:
+        for step in range(48):
+            for layer in range(L):
+                idx, _ = oracle.route(syn.router_logits(cfg, T, layer=layer, step=step).numpy(), k)
+                rows = {}
+                for e in idx.ravel():
+                    rows[int(e)] = rows.get(int(e), 0) + 1
+                m0 = ref.stats["misses"]
+                _run_step(cache, ref, layer, rows, lambda m: ecf.qstar_split(m, 0.4, 1.0))
+                if step >= 8:
+                    miss_lru += ref.stats["misses"] - m0
+                    miss_static += sum(1 for e in rows if e not in hot[layer])
+        assert {k2: v for k2, v in ecf.ecf_cache_get_stats(cache).items() if k2 != "dropped"} == ref.stats
+        for l in range(L):
+            for e in range(E):
+                s = ref.resident(l, e)
+                assert ecf.ecf_cache_slot_of(cache, l, e) == (-1 if s is None else s)
+        print(f"drifting trace: LRU {miss_lru} misses, first-phase static subset {miss_static}")
+        assert miss_lru < miss_static, (miss_lru, miss_static)
+    finally:
+        ecf.ecf_cache_destroy(cache)
