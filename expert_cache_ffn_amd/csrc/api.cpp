@@ -744,7 +744,10 @@ int forward_impl(const ecf_layer_args *a, const void *d_x, int32_t T, float *d_o
         // One token on the decode path, all experts resident, MXFP4 weights: the
         // down projection and the combine run as one kernel.
         const bool fused_down = !a->cache && path == ECF_PATH_DECODE && down_combine1_ok(s, T);
-        if ((rc = launch_route(s, lg, T, ro, stream)) != ECF_OK)
+        // One token on the decode path, all experts resident, bf16 activations: the
+        // gate/up GEMV derives the routing itself (no routing kernel).
+        const bool route1 = !a->cache && path == ECF_PATH_DECODE && gateup_route1_ok(s, T);
+        if (!route1 && (rc = launch_route(s, lg, T, ro, stream)) != ECF_OK)
             return rc;
 
         const float *host_part = nullptr;
@@ -754,10 +757,16 @@ int forward_impl(const ecf_layer_args *a, const void *d_x, int32_t T, float *d_o
             if ((rc = cache_step(a, d_x, T, ro, wl, ws, lay, path, stats, &tab, &host_part)) != ECF_OK)
                 return rc;
             ex.ptrs = tab;
-        } else if (fused_down) {
+        } else if (route1 || fused_down) {
             float *H = (float *)(ws + wl.hbuf);
-            if ((rc = launch_decode_gateup(s, ex, ro, d_x, T, H, stream)) != ECF_OK ||
-                (rc = launch_decode_down_combine1(s, ex, ro, H, a->d_residual, d_out, a->d_out_act, stream)) != ECF_OK)
+            rc = route1 ? launch_decode_gateup_route1(s, ex, lg, d_x, ro, H, stream)
+                        : launch_decode_gateup(s, ex, ro, d_x, T, H, stream);
+            if (rc != ECF_OK)
+                return rc;
+            rc = fused_down
+                     ? launch_decode_down_combine1(s, ex, ro, H, a->d_residual, d_out, a->d_out_act, stream)
+                     : launch_decode_down(s, ex, ro, H, T, (float *)(ws + wl.ybuf), stream);
+            if (rc != ECF_OK)
                 return rc;
         } else if ((rc = launch_experts(s, ex, ro, d_x, T, wl, ws, path, stream)) != ECF_OK) {
             return rc;

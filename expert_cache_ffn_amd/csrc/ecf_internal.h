@@ -110,6 +110,10 @@ int launch_prefill_gemm2(const ecf_shape &s, const ExpertTables &ex, const Route
 // One token (T = 1, k <= 8, MXFP4 weights with bf16 activations): the down
 // projection and the combine in one kernel, no Y in memory.
 bool down_combine1_ok(const ecf_shape &s, int T);
+// one token, bf16 activations, bf16 or MXFP4 weights: routing inside the gate/up GEMV
+bool gateup_route1_ok(const ecf_shape &s, int T);
+int launch_decode_gateup_route1(const ecf_shape &s, const ExpertTables &ex, const float *logits, const void *x,
+                                const RouteOut &o, float *H, hipStream_t st);
 int launch_decode_down_combine1(const ecf_shape &s, const ExpertTables &ex, const RouteOut &o, const float *H,
                                 const float *residual, float *out, void *out_act, hipStream_t st);
 int launch_combine(const ecf_shape &s, const ExpertTables &ex, const RouteOut &o, const float *Y, int T,

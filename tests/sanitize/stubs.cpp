@@ -10,6 +10,9 @@ int launch_route(const ecf_shape &, const float *, int, const RouteOut &, hipStr
 int launch_decode_gateup(const ecf_shape &, const ExpertTables &, const RouteOut &, const void *, int, float *,
                          hipStream_t) { std::abort(); }
 bool down_combine1_ok(const ecf_shape &, int) { return false; }
+bool gateup_route1_ok(const ecf_shape &, int) { return false; }
+int launch_decode_gateup_route1(const ecf_shape &, const ExpertTables &, const float *, const void *, const RouteOut &,
+                                float *, hipStream_t) { std::abort(); }
 int launch_decode_down_combine1(const ecf_shape &, const ExpertTables &, const RouteOut &, const float *, const float *,
                                 float *, void *, hipStream_t) { std::abort(); }
 int launch_decode_down(const ecf_shape &, const ExpertTables &, const RouteOut &, const float *, int, float *,
