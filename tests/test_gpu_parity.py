@@ -73,7 +73,7 @@ def test_auto_path_boundary_full_size(decode_cases, T, path):
 # ---- edge cases on small shapes -------------------------------------------------------
 
 @pytest.mark.parametrize("path", [ecf.ECF_PATH_DECODE, ecf.ECF_PATH_PREFILL])
-@pytest.mark.parametrize("E,k,T", [(1, 1, 5), (8, 8, 3), (8, 2, 1), (16, 4, 37)])
+@pytest.mark.parametrize("E,k,T", [(1, 1, 5), (8, 8, 3), (8, 2, 1), (16, 4, 37), (16, 6, 4), (8, 4, 2)])
 def test_small_shapes_both_paths(path, E, k, T):
     cfg = cfg_small(experts=E, top_k=k, cid=51 + E)
     say(f"case: small E={E} k={k} T={T} path={path}")
@@ -84,10 +84,12 @@ def test_small_shapes_both_paths(path, E, k, T):
 
 
 @pytest.mark.parametrize("E,k,T,path", [(1024, 32, 3, ecf.ECF_PATH_DECODE), (1024, 32, 80, ecf.ECF_PATH_DECODE),
-                                          (1024, 32, 80, ecf.ECF_PATH_PREFILL), (32, 32, 7, ecf.ECF_PATH_DECODE)])
+                                          (1024, 32, 80, ecf.ECF_PATH_PREFILL), (32, 32, 7, ecf.ECF_PATH_DECODE),
+                                          (1024, 32, 2, ecf.ECF_PATH_DECODE), (32, 32, 2, ecf.ECF_PATH_DECODE)])
 def test_largest_expert_count_and_topk(E, k, T, path):
     """The declared maxima (1024 experts, top-32) and k = E: 3 tokens route in the
-    single-block kernel, 80 tokens (2,560 rows) in the multi-block counting sort."""
+    single-block kernel, 80 tokens (2,560 rows) in the multi-block counting sort;
+    2 tokens with k = E = 32 put every expert on both tokens."""
     cfg = cfg_small(hidden=256, experts=E, top_k=k, inter=128, cid=140 + k + E % 7)
     say(f"case: E={E} k={k} T={T} path={path}")
     c = Case(cfg, T)
@@ -96,9 +98,9 @@ def test_largest_expert_count_and_topk(E, k, T, path):
     compare(res, c.oracle(), TOL["bf16"], f"E={E} k={k} T={T} path={path}")
 
 
-def test_tied_logits_pick_lowest_ids():
+@pytest.mark.parametrize("T", [4, 5])
+def test_tied_logits_pick_lowest_ids(T):
     cfg = cfg_small(logits="uniform", cid=60)
-    T = 5
     lg = torch.zeros((T, cfg.experts), dtype=torch.float32)
     lg[:, 5] = 1.0
     c = Case(cfg, T, logits=lg)
@@ -107,12 +109,13 @@ def test_tied_logits_pick_lowest_ids():
     compare(res, c.oracle(), TOL["bf16"], "ties")
 
 
-@pytest.mark.parametrize("T,renorm", [(20, 1), (20, 0), (600, 1), (600, 0)])
+@pytest.mark.parametrize("T,renorm", [(4, 1), (4, 0), (20, 1), (20, 0), (600, 1), (600, 0)])
 def test_special_logits(T, renorm):
     """NaN logits rank as -inf (in the order and in the softmax), -0 ties +0 with
     the lower id first, and -inf entries are picked after every finite logit, in
     id order: on the single-block routing kernel (T*k <= 2048, decode path) and
-    on the multi-block top-k and counting sort (T*k > 2048, prefill path)."""
+    on the multi-block top-k and counting sort (T*k > 2048, prefill path).  The
+    one-token routing inside the gate/up GEMV has its own cases below."""
     E, k = 16, 4
     cfg = cfg_small(experts=E, top_k=k, cid=140)
     rng = np.random.default_rng(140 + T)
@@ -134,6 +137,41 @@ def test_special_logits(T, renorm):
     ref = c.oracle()
     assert list(ref["idx"][1][:2]) == [3, 9] and list(ref["idx"][2]) == [2, 11, 5, 0]
     compare(res, ref, TOL["bf16"], f"special logits T={T} renorm={renorm}")
+
+
+@pytest.mark.parametrize("w", ["bf16", "mxfp4"])
+@pytest.mark.parametrize("renorm", [1, 0])
+def test_special_logits_one_token(w, renorm):
+    """The same special logits, one token per call, on the one-token decode path
+    (the routing inside the gate/up GEMV): NaN at the lowest id and inside the
+    range, -0 tying +0 at the top, and a top-k that has to take -inf / NaN
+    entries in id order."""
+    E, k = 16, 4
+    cfg = cfg_small(experts=E, top_k=k, w_dtype=w, cid=150)
+    rng = np.random.default_rng(150)
+    rows = []
+    for r in range(3):
+        lg = rng.normal(0, 1, (1, E)).astype(np.float32)
+        if r == 0:
+            lg[0, [0, 7]] = np.nan
+        elif r == 1:
+            lg[0] = -np.abs(lg[0]) - 1.0
+            lg[0, 3], lg[0, 9] = -0.0, 0.0
+        else:
+            lg[0] = -np.inf
+            lg[0, [2, 5, 11]] = [0.3, -0.1, 0.3]
+            lg[0, 1] = np.nan
+        rows.append(lg)
+    for r, lg in enumerate(rows):
+        say(f"case: special logits, one token, row type {r}, w={w}, renorm={renorm}")
+        c = Case(cfg, 1, renorm=renorm, logits=torch.from_numpy(lg))
+        res = c.run(path=ecf.ECF_PATH_DECODE)
+        ref = c.oracle()
+        if r == 1:
+            assert list(ref["idx"][0][:2]) == [3, 9]
+        if r == 2:
+            assert list(ref["idx"][0]) == [2, 11, 5, 0]
+        compare(res, ref, TOL["bf16"] if w == "bf16" else MX_DECODE_TOL, f"special logits, one token, type {r}")
 
 
 def test_no_renorm_gates():
@@ -316,7 +354,8 @@ def test_prefill_mxfp4_full_size_stratified():
 MX_DECODE_TOL = 1e-4
 
 
-@pytest.mark.parametrize("T,E,k,I", [(1, 8, 2, 192), (5, 8, 8, 256), (16, 16, 4, 128), (37, 8, 2, 64)])
+@pytest.mark.parametrize("T,E,k,I", [(1, 8, 2, 192), (5, 8, 8, 256), (16, 16, 4, 128), (37, 8, 2, 64),
+                                     (3, 8, 8, 128), (4, 16, 6, 256), (2, 32, 8, 512)])
 def test_decode_mxfp4_small(T, E, k, I):
     cfg = cfg_small(experts=E, top_k=k, inter=I, w_dtype="mxfp4", cid=110 + E + I // 64)
     say(f"case: decode mxfp4 T={T} E={E} k={k} I={I}")
